@@ -1,0 +1,194 @@
+"""Python binding of libfp8ds: delayed-scaling FP8 quantize and scaled FP8 GEMM
+for MI355X (gfx950).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  The
+binding refuses to run when the built library is missing; there is no CPU
+fallback.
+
+Entry points (same names as the C ABI in include/fp8ds.h):
+    scale_ring_bytes(hist_len)
+    scale_ring_init(ring, hist_len, fmt, init_scale=1.0)
+    fp8_quantize(x_bf16, fmt, ring, out=None)
+    fp8_mm(a, b, ..., out=None)
+plus ScaleRing (a ring in a torch uint8 device tensor) and read_ring().
+"""
+import ctypes
+import os
+import struct
+
+import torch
+
+E4M3 = 0
+E5M2 = 1
+NT, NN, TN = 0, 1, 2
+BIAS_NONE, BIAS_BF16, BIAS_F32 = 0, 1, 2
+TILES = {"256x256": 0, "128x128": 1, "64x64": 2}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8ds.so")
+_lib = None
+
+
+class Fp8dsError(RuntimeError):
+    pass
+
+
+class _MmArgs(ctypes.Structure):
+    _fields_ = [
+        ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
+        ("fmt_a", ctypes.c_int), ("fmt_b", ctypes.c_int), ("layout", ctypes.c_int), ("bias_kind", ctypes.c_int),
+        ("m", ctypes.c_int64), ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("batch", ctypes.c_int64),
+        ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
+        ("stride_a", ctypes.c_int64), ("stride_b", ctypes.c_int64), ("stride_c", ctypes.c_int64),
+        ("a_scale_inv", ctypes.c_void_p), ("b_scale_inv", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    """The loaded libfp8ds.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise Fp8dsError(f"{LIB_PATH} is missing: build it with "
+                             "`python delayed_scaling_amd/build.py` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.fp8_scale_ring_bytes.restype = ctypes.c_size_t
+        L.fp8_scale_ring_bytes.argtypes = [ctypes.c_int]
+        L.fp8_ring_scale_inv.restype = ctypes.c_void_p
+        L.fp8_ring_scale_inv.argtypes = [ctypes.c_void_p]
+        L.scale_ring_init.restype = ctypes.c_int
+        L.scale_ring_init.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+        L.fp8_quantize.restype = ctypes.c_int
+        L.fp8_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+        L.fp8_mm.restype = ctypes.c_int
+        L.fp8_mm.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_void_p]
+        L.fp8_mm_with_tile.restype = ctypes.c_int
+        L.fp8_mm_with_tile.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_void_p]
+        L.fp8_last_error.restype = ctypes.c_char_p
+        L.fp8_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise Fp8dsError(f"status {status}: {lib().fp8_last_error().decode()}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def scale_ring_bytes(hist_len):
+    return int(lib().fp8_scale_ring_bytes(int(hist_len)))
+
+
+def scale_ring_init(ring, hist_len, fmt, init_scale=1.0, stream=None):
+    """Initialise `ring` (a uint8 device tensor of scale_ring_bytes bytes)."""
+    _check(lib().scale_ring_init(_ptr(ring), int(hist_len), int(fmt), float(init_scale), _stream(stream)))
+
+
+class ScaleRing:
+    """A scale ring held in a torch uint8 device tensor."""
+
+    def __init__(self, hist_len, fmt, init_scale=1.0, device="cuda", stream=None):
+        n = scale_ring_bytes(hist_len)
+        if n == 0:
+            raise Fp8dsError(f"hist_len {hist_len} outside [1, 1024]")
+        self.hist_len, self.fmt = int(hist_len), int(fmt)
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        scale_ring_init(self.buf, hist_len, fmt, init_scale, stream)
+
+    def scale_inv_ptr(self):
+        """Device address of scale_inv_used (what fp8_mm dequantizes with)."""
+        return lib().fp8_ring_scale_inv(ctypes.c_void_p(self.buf.data_ptr()))
+
+    def read(self):
+        return read_ring(self.buf)
+
+
+def read_ring(buf):
+    """Copy a ring to the host and decode its fields (layout of include/fp8ds.h)."""
+    raw = buf.detach().cpu().numpy().tobytes()
+    scale, sinv, amax_last, idx, hist_len, fmt, status, _r0, amax_bits, ticket = struct.unpack_from("<fffiiiIIII", raw, 0)
+    hist = list(struct.unpack_from(f"<{hist_len}f", raw, 64)) if 1 <= hist_len <= 1024 else []
+    hist_bits = list(struct.unpack_from(f"<{hist_len}I", raw, 64)) if 1 <= hist_len <= 1024 else []
+    return {"scale": scale, "scale_inv_used": sinv, "amax_last": amax_last, "idx": idx,
+            "hist_len": hist_len, "fmt": fmt, "status": status, "amax_bits": amax_bits,
+            "ticket": ticket, "hist": hist, "hist_bits": hist_bits,
+            "scale_bits": struct.unpack_from("<I", raw, 0)[0],
+            "scale_inv_used_bits": struct.unpack_from("<I", raw, 4)[0],
+            "amax_last_bits": struct.unpack_from("<I", raw, 8)[0]}
+
+
+def fp8_quantize(x, fmt, ring, out=None, stream=None):
+    """Quantize bf16 tensor x with the ring's scale into uint8 codes; advances the ring."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise Fp8dsError("x must be a contiguous bf16 CUDA tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    rbuf = ring.buf if isinstance(ring, ScaleRing) else ring
+    _check(lib().fp8_quantize(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out), _stream(stream)))
+    return out
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return ctypes.c_void_p(x)
+    if isinstance(x, ScaleRing):
+        return ctypes.c_void_p(x.scale_inv_ptr())
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
+           batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
+           tile=None, stream=None):
+    """C = bf16(A @ B * a_scale_inv * b_scale_inv + bias) on uint8 fp8 code tensors.
+
+    a, b: uint8 device tensors holding the stored operands (see include/fp8ds.h
+    for the NT/NN/TN storage); a_scale_inv / b_scale_inv: ScaleRing, fp32 device
+    tensor or device address; bias: bf16 or fp32 device tensor [n] or None.
+    Leading dimensions and batch strides default to the dense layout.
+    """
+    a_cols = m if layout == TN else k
+    b_cols = k if layout == NT else n
+    a_rows = k if layout == TN else m
+    b_rows = n if layout == NT else k
+    lda = a_cols if lda is None else lda
+    ldb = b_cols if ldb is None else ldb
+    ldc = n if ldc is None else ldc
+    stride_a = a_rows * lda if stride_a is None else stride_a
+    stride_b = b_rows * ldb if stride_b is None else stride_b
+    stride_c = m * ldc if stride_c is None else stride_c
+    dev = a.device if a is not None else b.device
+    if out is None:
+        out = torch.empty(batch * stride_c if batch > 1 else m * ldc, dtype=torch.bfloat16, device=dev)
+    bias_kind = BIAS_NONE
+    if bias is not None:
+        bias_kind = {torch.bfloat16: BIAS_BF16, torch.float32: BIAS_F32}.get(bias.dtype)
+        if bias_kind is None:
+            raise Fp8dsError("bias must be bf16 or fp32")
+    args = _MmArgs(_addr(a), _addr(b), _addr(out), int(fmt_a), int(fmt_b), int(layout), bias_kind,
+                   int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
+                   int(stride_a), int(stride_b), int(stride_c),
+                   _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias))
+    if tile is None:
+        _check(lib().fp8_mm(ctypes.byref(args), _stream(stream)))
+    else:
+        t = TILES[tile] if isinstance(tile, str) else int(tile)
+        _check(lib().fp8_mm_with_tile(ctypes.byref(args), t, _stream(stream)))
+    return out
+
+
+__all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm",
+           "fp8_quantize", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH"]

@@ -1,0 +1,145 @@
+// C ABI of libfp8ds: argument validation, dispatch to the kernels, errors.
+// The declarations and their contracts are in include/fp8ds.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fp8ds.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* kernel_name) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(FP8DS_ELAUNCH, "%s: launch failed: %s", kernel_name, hipGetErrorString(e));
+  return FP8DS_OK;
+}
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_fmt(int f) { return f == FP8DS_E4M3 || f == FP8DS_E5M2; }
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+// Largest byte offset + 1 that one batch entry of a stored [rows][cols] view
+// with leading dimension ld touches, rounded up to 16.
+int64_t view_extent(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows == 0 || cols == 0) return 0;
+  const int64_t e = (rows - 1) * ld + cols;
+  return (e + 15) & ~int64_t(15);
+}
+
+}  // namespace
+}  // namespace fp8ds
+
+using namespace fp8ds;
+
+extern "C" {
+
+const char* fp8_last_error(void) { return g_err; }
+
+size_t fp8_scale_ring_bytes(int hist_len) {
+  if (hist_len < 1 || hist_len > FP8DS_RING_MAX_HIST) return 0;
+  return (size_t)FP8DS_RING_HEADER_BYTES + (((size_t)hist_len * 4 + 15) & ~(size_t)15);
+}
+
+const float* fp8_ring_scale_inv(const void* ring) {
+  return ring ? reinterpret_cast<const float*>(static_cast<const char*>(ring) + 4) : nullptr;
+}
+
+int scale_ring_init(void* ring, int hist_len, int fmt, float init_scale, void* stream) {
+  if (!ring) return set_error(FP8DS_EINVAL, "scale_ring_init: ring is NULL");
+  if (!aligned16(ring)) return set_error(FP8DS_EALIGN, "scale_ring_init: ring not 16-byte aligned");
+  if (hist_len < 1 || hist_len > FP8DS_RING_MAX_HIST)
+    return set_error(FP8DS_EINVAL, "scale_ring_init: hist_len %d outside [1, %d]", hist_len, FP8DS_RING_MAX_HIST);
+  if (!valid_fmt(fmt)) return set_error(FP8DS_EINVAL, "scale_ring_init: fmt %d is neither E4M3 (0) nor E5M2 (1)", fmt);
+  if (!(init_scale > 0.0f) || !(init_scale < __builtin_inff()))
+    return set_error(FP8DS_EINVAL, "scale_ring_init: init_scale must be finite and > 0");
+  return launch_ring_init(ring, hist_len, fmt, init_scale, static_cast<hipStream_t>(stream));
+}
+
+int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, void* stream) {
+  if (!valid_fmt(fmt)) return set_error(FP8DS_EINVAL, "fp8_quantize: fmt %d is neither E4M3 (0) nor E5M2 (1)", fmt);
+  if (numel < 0) return set_error(FP8DS_EINVAL, "fp8_quantize: numel %lld < 0", (long long)numel);
+  if (!ring) return set_error(FP8DS_EUNSUPPORTED, "fp8_quantize: ring is NULL (dynamic scaling is not provided)");
+  if (!aligned16(ring)) return set_error(FP8DS_EALIGN, "fp8_quantize: ring not 16-byte aligned");
+  if (numel == 0) return FP8DS_OK;
+  if (!x_bf16 || !y_fp8) return set_error(FP8DS_EINVAL, "fp8_quantize: x or y is NULL");
+  if (!aligned16(x_bf16) || !aligned16(y_fp8)) return set_error(FP8DS_EALIGN, "fp8_quantize: x or y not 16-byte aligned");
+  const uintptr_t xs = reinterpret_cast<uintptr_t>(x_bf16), ys = reinterpret_cast<uintptr_t>(y_fp8);
+  if (xs < ys + (uintptr_t)numel && ys < xs + 2 * (uintptr_t)numel)
+    return set_error(FP8DS_EINVAL, "fp8_quantize: x and y overlap");
+  return launch_quantize(x_bf16, numel, fmt, ring, y_fp8, 2048, static_cast<hipStream_t>(stream));
+}
+
+int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_tile(a, -1, stream); }
+
+int fp8_mm_with_tile(const fp8_mm_args* a, int tile, void* stream) {
+  if (!a) return set_error(FP8DS_EINVAL, "fp8_mm: args is NULL");
+  if (!valid_fmt(a->fmt_a) || !valid_fmt(a->fmt_b)) return set_error(FP8DS_EINVAL, "fp8_mm: bad fmt_a/fmt_b");
+  if (a->layout < FP8DS_NT || a->layout > FP8DS_TN) return set_error(FP8DS_EINVAL, "fp8_mm: bad layout %d", a->layout);
+  if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_F32)
+    return set_error(FP8DS_EINVAL, "fp8_mm: bad bias_kind %d", a->bias_kind);
+  const int64_t m = a->m, n = a->n, k = a->k, batch = a->batch == 0 ? 1 : a->batch;
+  if (m < 0 || n < 0 || k < 0 || batch < 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || batch > kMaxDim)
+    return set_error(FP8DS_EINVAL, "fp8_mm: dimensions must be in [0, 2^31)");
+  if (m == 0 || n == 0) return FP8DS_OK;
+  const bool tn = a->layout == FP8DS_TN;
+  const int64_t a_rows = tn ? k : m, a_cols = tn ? m : k;
+  const int64_t b_rows = a->layout == FP8DS_NT ? n : k, b_cols = a->layout == FP8DS_NT ? k : n;
+  if (!a->c || !a->a_scale_inv || !a->b_scale_inv) return set_error(FP8DS_EINVAL, "fp8_mm: c or a scale pointer is NULL");
+  if (k > 0 && (!a->a || !a->b)) return set_error(FP8DS_EINVAL, "fp8_mm: a or b is NULL");
+  if (a->bias_kind != FP8DS_BIAS_NONE && !a->bias) return set_error(FP8DS_EINVAL, "fp8_mm: bias_kind set but bias is NULL");
+  if (a->lda < (k > 0 ? a_cols : 0) || a->ldb < (k > 0 ? b_cols : 0) || a->ldc < n)
+    return set_error(FP8DS_EINVAL, "fp8_mm: leading dimension smaller than the row length");
+  if (a->stride_a < 0 || a->stride_b < 0 || a->stride_c < 0) return set_error(FP8DS_EINVAL, "fp8_mm: negative stride");
+  if (batch > 1 && a->stride_c < m * a->ldc) return set_error(FP8DS_EINVAL, "fp8_mm: stride_c smaller than one output");
+  if ((k > 0 && (!aligned16(a->a) || !aligned16(a->b))) || !aligned16(a->c) ||
+      (a->bias_kind != FP8DS_BIAS_NONE && !aligned16(a->bias)))
+    return set_error(FP8DS_EALIGN, "fp8_mm: a, b, c and bias must be 16-byte aligned");
+  if ((a->lda & 15) || (a->ldb & 15) || (a->ldc & 7) || (a->stride_a & 15) || (a->stride_b & 15) ||
+      (a->stride_c & 7))
+    return set_error(FP8DS_EALIGN, "fp8_mm: lda, ldb, strides of a/b must be multiples of 16, ldc and stride_c of 8");
+  const int64_t ext_a = k > 0 ? view_extent(a_rows, a_cols, a->lda) : 0;
+  const int64_t ext_b = k > 0 ? view_extent(b_rows, b_cols, a->ldb) : 0;
+  if (ext_a >= 0x80000000LL || ext_b >= 0x80000000LL)
+    return set_error(FP8DS_EUNSUPPORTED, "fp8_mm: one batch entry of an operand spans 2 GiB or more");
+  GemmProblem p{};
+  p.a = static_cast<const uint8_t*>(a->a);
+  p.b = static_cast<const uint8_t*>(a->b);
+  p.c = static_cast<uint16_t*>(a->c);
+  p.fmt_a = a->fmt_a;
+  p.fmt_b = a->fmt_b;
+  p.layout = a->layout;
+  p.bias_kind = a->bias_kind;
+  p.m = (int)m;
+  p.n = (int)n;
+  p.k = (int)k;
+  p.batch = (int)batch;
+  p.lda = a->lda;
+  p.ldb = a->ldb;
+  p.ldc = a->ldc;
+  p.stride_a = a->stride_a;
+  p.stride_b = a->stride_b;
+  p.stride_c = a->stride_c;
+  p.extent_a = (uint32_t)ext_a;
+  p.extent_b = (uint32_t)ext_b;
+  p.a_scale_inv = a->a_scale_inv;
+  p.b_scale_inv = a->b_scale_inv;
+  p.bias = a->bias;
+  return launch_gemm(p, tile, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,34 @@
+// Host-side launch helpers shared by the kernel files and the C ABI of libfp8ds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8ds {
+
+// Records a formatted message for fp8_last_error() and returns `code`.
+int set_error(int code, const char* fmt, ...);
+
+// Maps a failed kernel launch to FP8DS_ELAUNCH (status -4), else 0.
+int check_launch(const char* kernel_name);
+
+int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStream_t stream);
+int launch_quantize(const void* x, int64_t numel, int fmt, void* ring, void* y, int max_blocks, hipStream_t stream);
+
+struct GemmProblem {
+  const uint8_t* a;
+  const uint8_t* b;
+  uint16_t* c;
+  int fmt_a, fmt_b, layout, bias_kind;
+  int m, n, k, batch;
+  int64_t lda, ldb, ldc;
+  int64_t stride_a, stride_b, stride_c;
+  uint32_t extent_a, extent_b;   // bytes one batch entry of each operand spans, rounded up to 16
+  const float* a_scale_inv;
+  const float* b_scale_inv;
+  const void* bias;
+};
+
+int launch_gemm(const GemmProblem& p, int tile_override, hipStream_t stream);
+
+}  // namespace fp8ds

@@ -1,0 +1,234 @@
+// Delayed-scaling bf16 -> FP8 quantize with a fused amax and an in-kernel
+// scale-ring update (AstrAI history of astrai/extension/fp8.py @4dc5e923,
+// ring-finalize entry: the last block to finish folds the amax into the
+// history, reduces the window and publishes the next scale, so the update
+// costs no extra launch).
+//
+// One launch streams x once (16-byte loads, 8-byte stores), so the kernel is
+// bound by HBM: 3 bytes per element.  Each block reduces max|x| over its
+// elements, publishes it with one device-scope atomic max, and takes a ticket;
+// the block holding the last ticket finalizes the ring and resets the two
+// scratch words for the next call on the same stream.
+#include "device_common.h"
+#include "launch.h"
+
+namespace fp8ds {
+
+namespace {
+
+constexpr int kQBlock = 256;     // threads per block
+constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
+
+// Casts two products to the format's codes in the low or high half-word of
+// `word`.  Products are clamped to +-FMAX first because the hardware convert
+// is nearest-even but does not saturate; NaN is repaired by the caller.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pair(float a, float b, uint32_t word) {
+  if constexpr (FMT == kE4M3)
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
+  else
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)word, HI);
+}
+
+template <int FMT>
+__device__ __forceinline__ float clamp_fmax(float v) {
+  constexpr float m = FmtTraits<FMT>::kMax;
+  return fminf(fmaxf(v, -m), m);
+}
+
+// Quantizes 4 bf16 held in two 32-bit words into 4 codes packed in one word.
+template <int FMT>
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
+  const float f0 = __uint_as_float(w0 << 16), f1 = __uint_as_float(w0 & 0xFFFF0000u);
+  const float f2 = __uint_as_float(w1 << 16), f3 = __uint_as_float(w1 & 0xFFFF0000u);
+  const uint32_t out = cvt_pair<FMT, false>(clamp_fmax<FMT>(f0 * scale), clamp_fmax<FMT>(f1 * scale), 0u);
+  return cvt_pair<FMT, true>(clamp_fmax<FMT>(f2 * scale), clamp_fmax<FMT>(f3 * scale), out);
+}
+
+// A NaN element encodes as 0x7F with its sign; only chunks holding a NaN
+// take this path.
+__device__ __forceinline__ uint32_t fix_nan4(uint32_t w0, uint32_t w1, uint32_t codes) {
+  const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((h[i] & 0x7FFFu) > 0x7F80u) {
+      const uint32_t code = 0x7Fu | ((h[i] >> 8) & 0x80u);
+      codes = (codes & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return codes;
+}
+
+__device__ __forceinline__ uint32_t max_mag16(uint32_t w) {
+  const uint32_t m = w & 0x7FFF7FFFu;
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+template <int FMT>
+__device__ __forceinline__ void quant_chunk(v4u v, float scale, v2u& out, uint32_t& amax16) {
+  const uint32_t cm = max(max(max_mag16(v.x), max_mag16(v.y)), max(max_mag16(v.z), max_mag16(v.w)));
+  amax16 = max(amax16, cm);
+  out.x = quant4<FMT>(v.x, v.y, scale);
+  out.y = quant4<FMT>(v.z, v.w, scale);
+  if (cm > 0x7F80u) {                 // a NaN is present in this chunk
+    out.x = fix_nan4(v.x, v.y, out.x);
+    out.y = fix_nan4(v.z, v.w, out.y);
+  }
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Block-wide max; every thread gets the result.
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
+  v = wave_max(v);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < kQBlock / 64; ++i) r = max(r, red[i]);
+  return r;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict__ x, v2u* __restrict__ y,
+                                                           int64_t nchunk, const uint16_t* __restrict__ x_tail,
+                                                           uint8_t* __restrict__ y_tail, int tail,
+                                                           RingHeader* __restrict__ ring) {
+  __shared__ uint32_t red[kQBlock / 64];
+  __shared__ int s_last;
+  const float scale = ring->scale;
+  uint32_t amax16 = 0;
+
+  const int64_t step = (int64_t)gridDim.x * kQBlock * kQUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
+    if (base + (kQUnroll - 1) * kQBlock < nchunk) {
+      v4u v[kQUnroll];
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kQBlock);
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) {
+        v2u o;
+        quant_chunk<FMT>(v[u], scale, o, amax16);
+        __builtin_nontemporal_store(o, y + base + u * kQBlock);
+      }
+    } else {
+      for (int u = 0; u < kQUnroll; ++u) {
+        const int64_t c = base + u * kQBlock;
+        if (c < nchunk) {
+          v2u o;
+          quant_chunk<FMT>(x[c], scale, o, amax16);
+          y[c] = o;
+        }
+      }
+    }
+  }
+  // Elements past the last whole 8-element chunk.
+  if (tail > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int i = 0; i < tail; ++i) {
+      const uint32_t h = x_tail[i];
+      amax16 = max(amax16, h & 0x7FFFu);
+      const float v = clamp_fmax<FMT>(__uint_as_float(h << 16) * scale);
+      uint32_t code = cvt_pair<FMT, false>(v, 0.0f, 0u) & 0xFFu;
+      if ((h & 0x7FFFu) > 0x7F80u) code = 0x7Fu | ((h >> 8) & 0x80u);
+      y_tail[i] = (uint8_t)code;
+    }
+  }
+
+  const uint32_t bmax = block_max(amax16, red) << 16;   // |x| as fp32 bits
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (t == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last block: fold, reduce the window, publish.
+  const uint32_t a = __hip_atomic_load(&ring->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  const int H = ring->hist_len;
+  const int idx = ring->idx;
+  const bool bad_header = H < 1 || H > 1024 || idx < 0 || idx >= H;
+  const bool fmt_mismatch = ring->fmt != FMT;
+  float* hist = reinterpret_cast<float*>(ring + 1);
+  uint32_t w = 0;
+  if (!bad_header) {
+    for (int j = threadIdx.x; j < H; j += kQBlock) w = max(w, j == idx ? a : __float_as_uint(hist[j]));
+  }
+  w = block_max(w, red);
+  if (threadIdx.x == 0) {
+    if (bad_header || fmt_mismatch) {
+      ring->status |= (bad_header ? kStatusBadHeader : 0u) | (fmt_mismatch ? kStatusFmtMismatch : 0u);
+    } else {
+      hist[idx] = __uint_as_float(a);
+      ring->idx = idx + 1 == H ? 0 : idx + 1;
+      float next = scale;
+      if (w > 0u && w < 0x7F800000u) {
+        const float t = FmtTraits<FMT>::kMax / __uint_as_float(w);
+        if (__float_as_uint(t) < 0x7F800000u) next = t;
+      }
+      ring->scale = next;
+      ring->scale_inv_used = 1.0f / scale;
+      ring->amax_last = __uint_as_float(a);
+    }
+    __hip_atomic_store(&ring->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&ring->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ __launch_bounds__(256) void ring_init_kernel(RingHeader* ring, int hist_len, int fmt, float init_scale) {
+  float* hist = reinterpret_cast<float*>(ring + 1);
+  for (int j = threadIdx.x; j < hist_len; j += blockDim.x) hist[j] = 0.0f;
+  if (threadIdx.x == 0) {
+    ring->scale = init_scale;
+    ring->scale_inv_used = 1.0f / init_scale;
+    ring->amax_last = 0.0f;
+    ring->idx = 0;
+    ring->hist_len = hist_len;
+    ring->fmt = fmt;
+    ring->status = 0u;
+    ring->reserved0 = 0u;
+    ring->amax_bits = 0u;
+    ring->ticket = 0u;
+    for (int i = 0; i < 6; ++i) ring->reserved1[i] = 0u;
+  }
+}
+
+}  // namespace
+
+int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStream_t stream) {
+  hipLaunchKernelGGL(ring_init_kernel, dim3(1), dim3(256), 0, stream, static_cast<RingHeader*>(ring), hist_len,
+                     fmt, init_scale);
+  return check_launch("ring_init_kernel");
+}
+
+int launch_quantize(const void* x, int64_t numel, int fmt, void* ring, void* y, int max_blocks, hipStream_t stream) {
+  const int64_t nchunk = numel / 8;
+  const int tail = (int)(numel % 8);
+  const int64_t per_block = (int64_t)kQBlock * kQUnroll;
+  int64_t blocks = (nchunk + per_block - 1) / per_block;
+  if (blocks < 1) blocks = 1;
+  if (blocks > max_blocks) blocks = max_blocks;
+  const v4u* xv = static_cast<const v4u*>(x);
+  v2u* yv = static_cast<v2u*>(y);
+  const uint16_t* xt = static_cast<const uint16_t*>(x) + nchunk * 8;
+  uint8_t* yt = static_cast<uint8_t*>(y) + nchunk * 8;
+  RingHeader* r = static_cast<RingHeader*>(ring);
+  if (fmt == kE4M3)
+    hipLaunchKernelGGL(quantize_kernel<kE4M3>, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, xv, yv, nchunk, xt,
+                       yt, tail, r);
+  else
+    hipLaunchKernelGGL(quantize_kernel<kE5M2>, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, xv, yv, nchunk, xt,
+                       yt, tail, r);
+  return check_launch("quantize_kernel");
+}
+
+}  // namespace fp8ds

@@ -1,0 +1,155 @@
+/*
+ * fp8ds: delayed-scaling FP8 quantize and scaled FP8 GEMM for AMD MI355X (gfx950).
+ *
+ * Plain C ABI: no C++ types, no exceptions, no allocation.  Every pointer
+ * argument named "device" is device memory owned by the caller; the library
+ * keeps no device state of its own.  All calls are asynchronous on the given
+ * HIP stream (a hipStream_t passed as void*; NULL = the default stream) and
+ * never synchronise with the host.  A call returns FP8DS_OK after launching,
+ * or a negative status having launched nothing; fp8_last_error() then holds a
+ * message for the calling thread.
+ *
+ * Page citations name the AstrAI commit-history page and the entry on it.
+ */
+#ifndef FP8DS_H
+#define FP8DS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* 8-bit formats: OCP E4M3FN (max 448, no infinities) for forward operands and
+ * OCP E5M2 (max 57344) for gradients (fp8.py history @4dc5e923: the grad ring
+ * is kept apart from x/w; the format enum is validated at the binding,
+ * fp8.py history @f4c44ebf, quantize split entry). */
+typedef enum { FP8DS_E4M3 = 0, FP8DS_E5M2 = 1 } fp8ds_fmt;
+
+/* Operand storage of C[M,N] = A[M,K] * B[K,N], all row-major views:
+ *   NT: A stored [M,K], B stored [N,K]  (both K-contiguous: linear forward)
+ *   NN: A stored [M,K], B stored [K,N]  (B crosswise: dX = G * W)
+ *   TN: A stored [K,M], B stored [K,N]  (A and B crosswise: dW = G^T * X)
+ * (gemm.cuh history @5e76fbd1: RowMajor/ColMajor layout tags; crosswise-A
+ * and crosswise-B entries.) */
+typedef enum { FP8DS_NT = 0, FP8DS_NN = 1, FP8DS_TN = 2 } fp8ds_layout;
+
+/* Bias storage (bias-fusion entry, fp8.py history @f4c44ebf): none, bf16[N]
+ * or fp32[N]; added in fp32 before the single bf16 rounding. */
+typedef enum { FP8DS_BIAS_NONE = 0, FP8DS_BIAS_BF16 = 1, FP8DS_BIAS_F32 = 2 } fp8ds_bias_kind;
+
+enum {
+  FP8DS_OK = 0,
+  FP8DS_EINVAL = -1,      /* null pointer, bad enum, negative or oversized dimension  */
+  FP8DS_EALIGN = -2,      /* base pointer or leading dimension not 16-byte aligned    */
+  FP8DS_EUNSUPPORTED = -3,/* valid request this build does not implement              */
+  FP8DS_ELAUNCH = -4      /* the HIP runtime rejected the kernel launch               */
+};
+
+/* ---------------------------------------------------------------------------
+ * Scale ring: the per-operand delayed-scaling state (fp8.py history
+ * @4dc5e923: one buffer packing the history, the scale and a counter; one
+ * ring per operand x, w, g).  Caller-owned device memory of
+ * fp8_scale_ring_bytes(hist_len) bytes, 16-byte aligned, laid out as:
+ *
+ *   offset  type     field
+ *   0       float    scale           multiplier the next quantize applies
+ *   4       float    scale_inv_used  1 / (scale the last quantize applied): the
+ *                                    GEMM's dequantization multiplier (scale
+ *                                    snapshot entry, fp8.py history @f4c44ebf)
+ *   8       float    amax_last       amax of the last quantized tensor
+ *   12      int32    idx             next history slot to write
+ *   16      int32    hist_len        window length H, 1..1024
+ *   20      int32    fmt             fp8ds_fmt the ring serves
+ *   24      uint32   status          sticky device-side error bits (see below)
+ *   28      uint32   (reserved, 0)
+ *   32      uint32   amax_bits       scratch: running max of |x| bits, 0 between calls
+ *   36      uint32   ticket          scratch: finished-block counter, 0 between calls
+ *   40..63           (reserved, 0)
+ *   64      float    hist[H]         amax history window
+ *
+ * The ring is the only state of the method: copying its bytes out and back
+ * checkpoints and restores it.  Calls that use one ring must be ordered on
+ * one stream; concurrent use of one ring is undefined.
+ * status bits: 1 = fp8_quantize fmt differed from the ring's fmt,
+ *              2 = ring header invalid (hist_len or idx out of range).
+ * A call that sets a status bit leaves the ring's scale, history and index
+ * unchanged; its output bytes are unspecified.
+ * ------------------------------------------------------------------------- */
+#define FP8DS_RING_HEADER_BYTES 64
+#define FP8DS_RING_MAX_HIST 1024
+
+/* Bytes of a ring with hist_len slots (rounded up to 16); 0 if hist_len is
+ * outside [1, 1024]. */
+size_t fp8_scale_ring_bytes(int hist_len);
+
+/* Device address of a ring's scale_inv_used field (ring + 4), for
+ * fp8_mm_args.a_scale_inv / b_scale_inv. */
+const float* fp8_ring_scale_inv(const void* ring);
+
+/* Initialise a ring on `stream`: zero history, idx 0, scale = init_scale,
+ * scale_inv_used = 1/init_scale (IEEE binary32), scratch and status zero.
+ * ring: device, fp8_scale_ring_bytes(hist_len) bytes, 16-byte aligned.
+ * init_scale must be finite and > 0 (the pages' "seed" of a ring, fp8.py
+ * history @4dc5e923, FP8TensorMeta entry). */
+int scale_ring_init(void* ring, int hist_len, int fmt, float init_scale, void* stream);
+
+/* Delayed-scaling quantize (fp8.py history @4dc5e923, ring-finalize entry;
+ * @f4c44ebf, quantize split and amax entries):
+ *   y[i] = saturate_round_nearest_even_fmt(fl32(x[i]) * scale)   for i < numel
+ * with scale = ring->scale read at launch, NaN -> 0x7F | sign.  In the same
+ * launch (last-block epilogue, no extra kernel) the ring is advanced:
+ *   a = max_i |x[i]| (fp32, before the cast); hist[idx] = a; idx = (idx+1) % H;
+ *   w = max(hist); if w finite and > 0 and FMAX/w finite: scale = FMAX/w;
+ *   scale_inv_used = 1/scale_used; amax_last = a.
+ * x: device bf16[numel], 16-byte aligned.  y: device uint8[numel] (fp8
+ * codes), 16-byte aligned, must not overlap x.  ring: an initialised ring of
+ * format fmt.  numel == 0 launches nothing and leaves the ring unchanged.
+ * ring == NULL (dynamic scaling) returns FP8DS_EUNSUPPORTED. */
+int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, void* stream);
+
+/* Scaled FP8 GEMM arguments.  Zero-initialise and set what you use: a
+ * zeroed field means "absent" (gemm.cuh history @5e76fbd1, null-default
+ * params entry). */
+typedef struct fp8_mm_args {
+  const void* a;            /* device fp8 codes, layout per `layout`                 */
+  const void* b;            /* device fp8 codes                                      */
+  void* c;                  /* device bf16 [batch][M][ldc] output                    */
+  int fmt_a, fmt_b;         /* fp8ds_fmt of each operand                             */
+  int layout;               /* fp8ds_layout                                          */
+  int bias_kind;            /* fp8ds_bias_kind                                       */
+  int64_t m, n, k;          /* problem size; each 0 .. 2^31-1                        */
+  int64_t batch;            /* number of products; 0 is treated as 1                 */
+  int64_t lda, ldb, ldc;    /* leading dimension of each stored view, in elements    */
+  int64_t stride_a, stride_b, stride_c; /* batch strides in elements; 0 broadcasts a/b */
+  const float* a_scale_inv; /* device fp32 scalar, e.g. fp8_ring_scale_inv(ring_a)   */
+  const float* b_scale_inv; /* device fp32 scalar                                    */
+  const void* bias;         /* device bf16[N] or fp32[N], broadcast over rows, batch */
+} fp8_mm_args;
+
+/* Scaled FP8 GEMM (gemm.cuh history @5e76fbd1; fp8.py history @f4c44ebf,
+ * bias-fusion and 3-D operand entries):
+ *   C[b][m][n] = bf16_rne( sum_k A_b[m,k] * B_b[k,n]  (fp32 accumulate)
+ *                          * (a_scale_inv * b_scale_inv) + fl32(bias[n]) )
+ * Alignment: a, b, c, bias 16-byte aligned; lda, ldb multiples of 16 and
+ * ldc a multiple of 8; batch strides multiples of 16 (a, b) and 8 (c).
+ * Each stored operand of one batch entry must span < 2^31 bytes.
+ * lda >= K (NT/NN) or >= M (TN); ldb >= K (NT) or >= N (NN/TN); ldc >= N.
+ * m == 0 or n == 0 launches nothing; k == 0 writes bf16(bias) (or 0).
+ * c must not overlap a, b or bias. */
+int fp8_mm(const fp8_mm_args* args, void* stream);
+
+/* fp8_mm with the workgroup tile forced: tile = index into the tile family
+ * (0: 256x256, 1: 128x128, 2: 64x64), -1 = the automatic choice.  Same
+ * results within the tolerance of fp8_mm; for tests and tuning sweeps. */
+int fp8_mm_with_tile(const fp8_mm_args* args, int tile, void* stream);
+
+/* Message of the last non-zero status returned on the calling thread. */
+const char* fp8_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8DS_H */

@@ -1,0 +1,91 @@
+"""The C ABI library loads on the host and exports every function that
+include/fp8ds.h declares; argument checks that return before any HIP call
+report the documented status codes.  CPU only: no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delayed_scaling_amd as ds
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ds.LIB_PATH):
+        pytest.fail("libfp8ds.so is not built (run __graft_entry__.build())")
+    return ds.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ["fp8_quantize", "fp8_mm", "scale_ring_init", "fp8_scale_ring_bytes", "fp8_last_error"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_ring_bytes(L):
+    assert ds.scale_ring_bytes(0) == 0
+    assert ds.scale_ring_bytes(1025) == 0
+    assert ds.scale_ring_bytes(1) == 64 + 16
+    assert ds.scale_ring_bytes(4) == 64 + 16
+    assert ds.scale_ring_bytes(16) == 64 + 64
+    assert ds.scale_ring_bytes(1024) == 64 + 4096
+    assert L.fp8_ring_scale_inv(ctypes.c_void_p(4096)) == 4100
+
+
+def test_validation_errors_launch_nothing(L):
+    # each of these returns before touching the GPU
+    assert L.fp8_quantize(None, 16, 7, ctypes.c_void_p(64), None, None) == -1
+    assert b"fmt" in L.fp8_last_error()
+    assert L.fp8_quantize(None, -1, 0, ctypes.c_void_p(64), None, None) == -1
+    assert L.fp8_quantize(None, 16, 0, None, None, None) == -3
+    assert L.fp8_quantize(None, 16, 0, ctypes.c_void_p(65), None, None) == -2
+    assert L.fp8_quantize(None, 0, 0, ctypes.c_void_p(64), None, None) == 0      # empty: no-op
+    assert L.scale_ring_init(None, 4, 0, 1.0, None) == -1
+    assert L.scale_ring_init(ctypes.c_void_p(64), 0, 0, 1.0, None) == -1
+    assert L.scale_ring_init(ctypes.c_void_p(64), 4, 0, 0.0, None) == -1
+    assert L.scale_ring_init(ctypes.c_void_p(64), 4, 0, float("inf"), None) == -1
+    assert L.scale_ring_init(ctypes.c_void_p(72), 4, 0, 1.0, None) == -2
+    args = ds._MmArgs()
+    args.layout = 5
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
+    assert b"layout" in L.fp8_last_error()
+    args.layout = 0
+    args.m, args.n, args.k = 0, 16, 16
+    assert L.fp8_mm(ctypes.byref(args), None) == 0                                # empty: no-op
+    args.m = 16
+    assert L.fp8_mm(ctypes.byref(args), None) == -1                               # null pointers
+    args.a, args.b, args.c = 4096, 8192, 16384
+    args.a_scale_inv, args.b_scale_inv = 32768, 32768
+    args.lda, args.ldb, args.ldc = 8, 16, 16                                      # lda < K
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
+    args.lda = 24                                                                 # not a multiple of 16
+    assert L.fp8_mm(ctypes.byref(args), None) == -2
+    args.lda = 16
+    args.a = 4100                                                                 # misaligned base
+    assert L.fp8_mm(ctypes.byref(args), None) == -2
+    args.a = 4096
+    args.bias_kind = 1                                                            # bias kind without pointer
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
+    args.bias_kind = 0
+    args.m = 1 << 31
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
+    args.m, args.k, args.lda, args.ldb = 1 << 20, 1 << 12, 1 << 12, 1 << 12       # 4 GiB operand
+    assert L.fp8_mm(ctypes.byref(args), None) == -3
