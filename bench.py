@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the delayed-scaling FP8 hot path on one MI355X.
+
+One step = one pass of the path over one batch of synthetic input, the
+square 8192^3 workload: delayed-scaling quantize of A [8192, 8192] and of
+B [8192, 8192] (bf16 ~ N(0,1), E4M3, history 16, amax + ring update fused)
+followed by the scaled FP8 GEMM C = A8 * B8^T (NT, fp32 accumulate, bf16
+out).  Inputs are resident in HBM before timing starts; three copies of the
+inputs rotate so the 256 MB Infinity Cache cannot serve a step from the
+previous one.
+
+Prints one JSON line.  `value` is the step's GEMM FLOPs over the measured
+step time (both quantizes included), in TFLOP/s.  `roofline` is the GEMM
+kernel's own rate (HIP events around each launch, on the launch stream)
+against the dense FP8 MFMA peak; `roofline_quantize` the quantize kernel's
+against HBM.  `cpu_baseline` times the oracle (numpy) on a bounded slice of
+the same step on the host.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--size", type=int, default=8192, help="M = N = K of the square workload")
+    ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="output rows of the oracle sample")
+    return ap.parse_args()
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per GEMM launch recorded in profiles/ by the two PMC runs,
+    or None when the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(a_bits, b_bits, size, rows):
+    """The oracle as it stands on a bounded slice of the step: quantize all
+    of B and the first `rows` rows of A, then the first `rows` output rows of
+    the GEMM.  Scaled to the metric as GEMM FLOPs of the slice per second."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    ra = oracle.ring_init(16, oracle.E4M3)
+    rb = oracle.ring_init(16, oracle.E4M3)
+    qa, ra = oracle.quantize_step(ra, a_bits[:rows])
+    qb, rb = oracle.quantize_step(rb, b_bits)
+    oracle.mm(qa.reshape(-1), qb.reshape(-1), 0, 0, oracle.NT, rows, size, size, size, size,
+              ra.scale_inv_used, rb.scale_inv_used)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * size * size
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"first {rows} of {size} output rows: quantize B ({size}x{size}) and {rows} rows of A, "
+                       f"fp64 GEMM of the slice; {dt:.1f} s; numpy elementwise steps on 1 thread, "
+                       f"the fp64 matmul on {blas_threads} BLAS threads")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import delayed_scaling_amd as ds
+    from synth import bf16_normal, seed_for
+
+    n = args.size
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    a_bits = bf16_normal((n, n), seed_for(3, 0, "A"))
+    b_bits = bf16_normal((n, n), seed_for(3, 0, "B"))
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    a0, b0 = to_dev(a_bits), to_dev(b_bits)
+    rot = max(1, args.rotate)
+    A = [a0] + [a0.clone() for _ in range(rot - 1)]
+    B = [b0] + [b0.clone() for _ in range(rot - 1)]
+    A8 = [torch.empty((n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    B8 = [torch.empty((n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    C = [torch.empty((n, n), dtype=torch.bfloat16, device=dev) for _ in range(rot)]
+    ring_a = ds.ScaleRing(16, ds.E4M3)
+    ring_b = ds.ScaleRing(16, ds.E4M3)
+
+    # Calibration copy of known size for the HBM counters (a device-to-device
+    # copy of 256 MiB, read once and written once).
+    cal_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+
+    def step(i, ev=None):
+        r = i % rot
+        if ev is not None:
+            ev[0].record(stream)
+        ds.fp8_quantize(A[r], ds.E4M3, ring_a, out=A8[r])
+        if ev is not None:
+            ev[1].record(stream)
+        ds.fp8_quantize(B[r], ds.E4M3, ring_b, out=B8[r])
+        if ev is not None:
+            ev[2].record(stream)
+        ds.fp8_mm(A8[r], B8[r], ds.E4M3, ds.E4M3, ds.NT, n, n, n, ring_a, ring_b, out=C[r])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    q_ms = [(e[0].elapsed_time(e[1]) + e[1].elapsed_time(e[2])) / 2 for e in events]
+    g_ms = [e[2].elapsed_time(e[3]) for e in events]
+    q_avg = sum(q_ms) / len(q_ms)
+    g_avg = sum(g_ms) / len(g_ms)
+    flops = 2.0 * n * n * n
+    q_bytes = 3.0 * n * n
+    gemm_tflops = flops / (g_avg * 1e-3) / 1e12
+    q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
+    traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip"))
+
+    out = {
+        "metric": "FP8 GEMM TFLOP/s (E4M3 NT 8192^3) + quantize GB/s, % of MI355X peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": f"square E4M3 NT {n}^3: delayed-scaling quantize of A and B ({n}x{n} bf16 "
+                               f"~N(0,1), history 16) + scaled FP8 GEMM, bf16 out, no bias",
+                   "m": n, "n": n, "k": n, "hist_len": 16, "input_rotation": rot},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "gemm_kernel<256,256,NT,E4M3,E4M3>",
+                     "avg_launch_us": round(g_avg * 1e3, 2)},
+        "roofline_quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
+                              "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
+                              "kernel": "quantize_kernel<E4M3>", "bytes_per_launch": q_bytes,
+                              "avg_launch_us": round(q_avg * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(a_bits, b_bits, n, min(args.cpu_rows, n))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

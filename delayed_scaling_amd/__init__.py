@@ -62,6 +62,9 @@ def lib():
         L.fp8_quantize.restype = ctypes.c_int
         L.fp8_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                    ctypes.c_void_p, ctypes.c_void_p]
+        L.fp8_quantize_with_grid.restype = ctypes.c_int
+        L.fp8_quantize_with_grid.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm.restype = ctypes.c_int
         L.fp8_mm.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_void_p]
         L.fp8_mm_with_tile.restype = ctypes.c_int
@@ -129,14 +132,18 @@ def read_ring(buf):
             "amax_last_bits": struct.unpack_from("<I", raw, 8)[0]}
 
 
-def fp8_quantize(x, fmt, ring, out=None, stream=None):
+def fp8_quantize(x, fmt, ring, out=None, stream=None, max_blocks=None):
     """Quantize bf16 tensor x with the ring's scale into uint8 codes; advances the ring."""
     if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
         raise Fp8dsError("x must be a contiguous bf16 CUDA tensor")
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     rbuf = ring.buf if isinstance(ring, ScaleRing) else ring
-    _check(lib().fp8_quantize(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out), _stream(stream)))
+    if max_blocks is None:
+        _check(lib().fp8_quantize(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out), _stream(stream)))
+    else:
+        _check(lib().fp8_quantize_with_grid(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out),
+                                            int(max_blocks), _stream(stream)))
     return out
 
 

@@ -4,7 +4,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/fp8ds.h"
+#include "fp8ds.h"
 #include "launch.h"
 
 namespace fp8ds {
@@ -71,6 +71,13 @@ int scale_ring_init(void* ring, int hist_len, int fmt, float init_scale, void* s
 }
 
 int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, void* stream) {
+  return fp8_quantize_with_grid(x_bf16, numel, fmt, ring, y_fp8, 0, stream);
+}
+
+int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, int max_blocks,
+                           void* stream) {
+  if (max_blocks < 0 || max_blocks > (1 << 20))
+    return set_error(FP8DS_EINVAL, "fp8_quantize: max_blocks %d outside [0, 2^20]", max_blocks);
   if (!valid_fmt(fmt)) return set_error(FP8DS_EINVAL, "fp8_quantize: fmt %d is neither E4M3 (0) nor E5M2 (1)", fmt);
   if (numel < 0) return set_error(FP8DS_EINVAL, "fp8_quantize: numel %lld < 0", (long long)numel);
   if (!ring) return set_error(FP8DS_EUNSUPPORTED, "fp8_quantize: ring is NULL (dynamic scaling is not provided)");
@@ -81,7 +88,7 @@ int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y
   const uintptr_t xs = reinterpret_cast<uintptr_t>(x_bf16), ys = reinterpret_cast<uintptr_t>(y_fp8);
   if (xs < ys + (uintptr_t)numel && ys < xs + 2 * (uintptr_t)numel)
     return set_error(FP8DS_EINVAL, "fp8_quantize: x and y overlap");
-  return launch_quantize(x_bf16, numel, fmt, ring, y_fp8, 2048, static_cast<hipStream_t>(stream));
+  return launch_quantize(x_bf16, numel, fmt, ring, y_fp8, max_blocks, static_cast<hipStream_t>(stream));
 }
 
 int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_tile(a, -1, stream); }

@@ -54,8 +54,43 @@ struct FmtTraits<kE5M2> {
 
 // Raw buffer resource over `bytes` bytes from `base`; loads at offsets at or
 // beyond `bytes` return zero (the word-3 constant selects 32-bit raw access).
+// Both arguments must be uniform across the wave: they are moved to scalar
+// registers explicitly, so the descriptor never needs a per-lane loop.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// The four words of a raw buffer descriptor in scalar registers, for the
+// inline-asm LDS loads below (base, stride 0, size in bytes, 32-bit raw format).
+__device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return v4i{(int)__builtin_amdgcn_readfirstlane((uint32_t)b),
+             (int)(__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) & 0xFFFFu),
+             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at `voff` in the
+// buffer land at LDS byte lds_base + 16 * lane (lds_base wave-uniform); an
+// offset at or past the buffer size lands as zeros.  Written as inline asm so
+// the compiler does not guard every later LDS read with a wait for all
+// outstanding loads: callers count these loads themselves (vmcnt) and order
+// LDS through barriers.  The instruction writes no VGPR.
+__device__ __forceinline__ void load_lds16(v4i rsrc, uint32_t lds_base, uint32_t voff) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ uint32_t lds_address(const lds_char_t* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>(p);
 }
 
 }  // namespace fp8ds

@@ -34,7 +34,8 @@ namespace fp8ds {
 
 namespace {
 
-constexpr int kBK = 128;          // K bytes (= elements) per stage
+constexpr int kBK = 64;           // K bytes (= elements) per pipeline stage
+constexpr int kStages = 4;        // LDS stages in flight
 constexpr int kThreads = 256;     // 4 waves
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every buffer: loads give zero
 
@@ -54,13 +55,14 @@ struct GemmKArgs {
   int bias_kind;
 };
 
-// K-contiguous tile [rows][128 B]: 16-byte chunk c of row r sits at chunk
-// c ^ swz_k(r).  Sixteen consecutive rows reading one logical chunk then hit
-// sixteen different 16-byte bank groups (and any eight consecutive rows hit
-// eight), whichever of 32 or 64 banks the LDS serves per clock.
-__device__ __forceinline__ int swz_k(int r) { return (r ^ (r >> 3)) & 7; }
+// K-contiguous tile [rows][64 B]: 16-byte chunk c of row r sits at chunk
+// c ^ swz_k(r).  A fragment read (32 consecutive rows, lanes l and l+32
+// taking adjacent chunk pairs of one row) is then free of LDS bank conflicts;
+// the choice was measured on gfx950 (SQ_LDS_BANK_CONFLICT = 0), where the
+// xor of (r >> 1) ^ (r >> 3) still left 4 conflict cycles per ds_read_b128.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
 
-// MN-contiguous tile [128 k][R chunks]: chunk c of row k sits at c ^ swz_mn(k).
+// MN-contiguous tile [64 k][R chunks]: chunk c of row k sits at c ^ swz_mn(k).
 // A transpose read touches 8 consecutive rows x 2 adjacent chunks; the
 // swizzle spreads them over distinct bank groups.
 template <int R>
@@ -90,28 +92,28 @@ __device__ __forceinline__ void map_tile(const GemmKArgs& p, int& bt, int& tm, i
 }
 
 // 32 rows x 64 k of a K-contiguous tile: lane l gets row base + l%32,
-// k = 64*s + 32*(l/32) + [0, 32).
-__device__ __forceinline__ v8i frag_k(const lds_char_t* tile, int base, int s, int lane) {
+// k = 32*(l/32) + [0, 32).
+__device__ __forceinline__ v8i frag_k(const lds_char_t* tile, int base, int lane) {
   const int row = base + (lane & 31);
-  const int c0 = 4 * s + 2 * (lane >> 5);
+  const int c0 = 2 * (lane >> 5);
   const int sw = swz_k(row);
   const v4i lo = *(const lds_v4i_t*)(tile + row * kBK + ((c0 ^ sw) << 4));
   const v4i hi = *(const lds_v4i_t*)(tile + row * kBK + (((c0 + 1) ^ sw) << 4));
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// The same fragment from an MN-contiguous tile [128 k][R*16 B] through four
-// transpose reads: read t hands lane l the bytes k = 64*s + 32*(l/32) + 8*t + [0, 8)
+// The same fragment from an MN-contiguous tile [64 k][R*16 B] through four
+// transpose reads: read t hands lane l the bytes k = 32*(l/32) + 8*t + [0, 8)
 // of column base + l%32.  Within each 16-lane group, the even lanes address
 // rows k..k+7 at the group's first 8 columns and the odd lanes the next 8.
 template <int R>
-__device__ __forceinline__ v8i frag_mn(const lds_char_t* tile, int base, int s, int lane) {
+__device__ __forceinline__ v8i frag_mn(const lds_char_t* tile, int base, int lane) {
   const int q = lane & 15;
   const int cl = (base >> 4) + ((lane >> 4) & 1);
   v2i part[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int kr = 64 * s + 32 * (lane >> 5) + 8 * t + (q >> 1);
+    const int kr = 32 * (lane >> 5) + 8 * t + (q >> 1);
     const int addr = kr * (R * 16) + ((cl ^ swz_mn<R>(kr)) << 4) + 8 * (q & 1);
     part[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(tile + addr));
   }
@@ -119,9 +121,9 @@ __device__ __forceinline__ v8i frag_mn(const lds_char_t* tile, int base, int s, 
 }
 
 template <bool KC, int ROWS>
-__device__ __forceinline__ v8i load_frag(const lds_char_t* tile, int base, int s, int lane) {
-  if constexpr (KC) return frag_k(tile, base, s, lane);
-  else return frag_mn<ROWS / 16>(tile, base, s, lane);
+__device__ __forceinline__ v8i load_frag(const lds_char_t* tile, int base, int lane) {
+  if constexpr (KC) return frag_k(tile, base, lane);
+  else return frag_mn<ROWS / 16>(tile, base, lane);
 }
 
 // Per-lane byte offset of load slot `slot` of an operand tile, for k0 = 0;
@@ -130,7 +132,7 @@ __device__ __forceinline__ v8i load_frag(const lds_char_t* tile, int base, int s
 template <bool KC, int ROWS>
 __device__ __forceinline__ uint32_t slot_offset(int slot, int mn0, int mn_lim, uint32_t ld, int& kpos) {
   if constexpr (KC) {
-    const int row = slot >> 3, pch = slot & 7, lch = pch ^ swz_k(row);
+    const int row = slot >> 2, pch = slot & 3, lch = pch ^ swz_k(row);
     kpos = lch << 4;
     return mn0 + row < mn_lim ? (uint32_t)row * ld + (uint32_t)(lch << 4) : kOOB;
   } else {
@@ -146,14 +148,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `stages` stages of LPS loads each are still in flight.
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int stages) {
+  static_assert(LPS * (kStages - 1) <= 63, "vmcnt holds at most 63");
+  if (stages >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPS));
+  else if (stages == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
+  else if (stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// Workgroup barrier ordering LDS only: outstanding global->LDS prefetches of
+// later stages stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, int OCC>
 __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK, STAGE = A_BYTES + B_BYTES;
   constexpr int A_LOADS = A_BYTES / 1024 / 4, B_LOADS = B_BYTES / 1024 / 4;
+  constexpr int LPS = A_LOADS + B_LOADS;
   static_assert(TM >= 1 && TN >= 1 && A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * STAGE];
   lds_char_t* smem = (lds_char_t*)smem_raw;
 
   const int lane = threadIdx.x & 63;
@@ -179,24 +204,38 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   for (int j = 0; j < B_LOADS; ++j)
     b_voff[j] = slot_offset<B_KC, BN>((j * 4 + wave) * 64 + lane, n0, p.n, p.ldb, b_kpos[j]);
 
-  auto issue = [&](int kt, int st, bool tail) {
+  // Global -> LDS loads of K stage kt into LDS buffer kt % kStages.
+  auto issue = [&](int kt, bool tail) __attribute__((always_inline)) {
     const int k0 = kt * kBK;
     const int klim = p.k - k0;
     const uint32_t a_adv = A_KC ? (uint32_t)k0 : (uint32_t)k0 * p.lda;
     const uint32_t b_adv = B_KC ? (uint32_t)k0 : (uint32_t)k0 * p.ldb;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_tile + a_adv, a_rem > a_adv ? a_rem - a_adv : 0u);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_tile + b_adv, b_rem > b_adv ? b_rem - b_adv : 0u);
-    lds_char_t* sa = smem + st * STAGE;
-    lds_char_t* sb = sa + A_BYTES;
+    const v4i ra = rsrc_words(a_tile + a_adv, a_rem > a_adv ? a_rem - a_adv : 0u);
+    const v4i rb = rsrc_words(b_tile + b_adv, b_rem > b_adv ? b_rem - b_adv : 0u);
+    const uint32_t la = lds_address(smem + (kt % kStages) * STAGE) + wave * 1024;
+    const uint32_t lb = la + A_BYTES;
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) {
-      const uint32_t off = (tail && a_kpos[j] >= klim) ? kOOB : a_voff[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + (j * 4 + wave) * 1024), 16, off, 0, 0, 0);
-    }
+    for (int j = 0; j < A_LOADS; ++j)
+      load_lds16(ra, la + j * 4096, (tail && a_kpos[j] >= klim) ? kOOB : a_voff[j]);
 #pragma unroll
-    for (int j = 0; j < B_LOADS; ++j) {
-      const uint32_t off = (tail && b_kpos[j] >= klim) ? kOOB : b_voff[j];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + (j * 4 + wave) * 1024), 16, off, 0, 0, 0);
+    for (int j = 0; j < B_LOADS; ++j)
+      load_lds16(rb, lb + j * 4096, (tail && b_kpos[j] >= klim) ? kOOB : b_voff[j]);
+  };
+
+  // The chunk holding K's last bytes also holds the row's padding; zero the
+  // bytes at or past K in the K-contiguous tiles of the last stage (one row
+  // per thread, at most 15 bytes each).
+  auto zero_k_padding = [&](int kt) __attribute__((always_inline)) {
+    const int kin = p.k - kt * kBK;
+    const int c_lo = kin & ~15;
+    lds_char_t* sa = smem + (kt % kStages) * STAGE;
+    constexpr int ROWS = (A_KC ? BM : 0) + (B_KC ? BN : 0);
+    for (int r = threadIdx.x; r < ROWS; r += kThreads) {
+      const bool in_a = A_KC && r < BM;
+      const int row = in_a || !A_KC ? r : r - BM;
+      lds_char_t* rp = sa + (in_a ? 0 : A_BYTES) + row * kBK + (((c_lo >> 4) ^ swz_k(row)) << 4) - c_lo;
+#pragma nounroll
+      for (int b = kin; b < c_lo + 16; ++b) rp[b] = 0;
     }
   };
 
@@ -206,50 +245,76 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
 #pragma unroll
     for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
 
-  const int kt_total = (p.k + kBK - 1) / kBK;
-  const int kt_full = p.k / kBK;
-  if (kt_total > 0) issue(0, 0, kt_full == 0);
-
-  for (int kt = 0; kt < kt_total; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of stage kt are in LDS
-    __syncthreads();                      // everyone's are; everyone is done with stage kt-1
-    const int st = kt & 1;
-    if (kt == kt_full && (p.k & 15) != 0) {
-      // The chunk holding K's last bytes also holds the row's padding; zero
-      // the bytes at or past K in K-contiguous tiles of the last stage.
-      const int kin = p.k - kt * kBK;
-      const int c_lo = kin & ~15, c_hi = c_lo + 16;
-      if constexpr (A_KC) {
-        for (int row = threadIdx.x; row < BM; row += kThreads) {
-          lds_char_t* rp = smem + st * STAGE + row * kBK + (((c_lo >> 4) ^ swz_k(row)) << 4);
-          for (int b = kin; b < c_hi; ++b) rp[b - c_lo] = 0;
-        }
-      }
-      if constexpr (B_KC) {
-        for (int row = threadIdx.x; row < BN; row += kThreads) {
-          lds_char_t* rp = smem + st * STAGE + A_BYTES + row * kBK + (((c_lo >> 4) ^ swz_k(row)) << 4);
-          for (int b = kin; b < c_hi; ++b) rp[b - c_lo] = 0;
-        }
-      }
-      __syncthreads();
-    }
-    if (kt + 1 < kt_total) issue(kt + 1, st ^ 1, kt + 1 >= kt_full);
-
-    const lds_char_t* sa = smem + st * STAGE;
+  // Fragments of two consecutive stages live in registers: while the MFMAs
+  // of stage kt run, the LDS reads of stage kt+1 and the global loads of
+  // stage kt+kStages are in flight.
+  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  auto read_frags = [&](int kt, v8i (&fa)[TM], v8i (&fb)[TN]) __attribute__((always_inline)) {
+    const lds_char_t* sa = smem + (kt % kStages) * STAGE;
     const lds_char_t* sb = sa + A_BYTES;
 #pragma unroll
-    for (int s = 0; s < kBK / 64; ++s) {
-      v8i af[TM], bf[TN];
+    for (int i = 0; i < TM; ++i) fa[i] = load_frag<A_KC, BM>(sa, wm * WM + i * 32, lane);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = load_frag<A_KC, BM>(sa, wm * WM + i * 32, s, lane);
+    for (int i = 0; i < TN; ++i) fb[i] = load_frag<B_KC, BN>(sb, wn * WN + i * 32, lane);
+  };
+  auto mfmas = [&](const v8i (&fa)[TM], const v8i (&fb)[TN]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < TN; ++i) bf[i] = load_frag<B_KC, BN>(sb, wn * WN + i * 32, s, lane);
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int i = 0; i < TN; ++i)
+      for (int j = 0; j < TM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+  };
+
+  const int kt_total = (p.k + kBK - 1) / kBK;
+  const int kt_full = p.k / kBK;
+  const bool kfix = (p.k & 15) != 0;
 #pragma unroll
-        for (int j = 0; j < TM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf[i], af[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+  for (int s = 0; s < kStages; ++s)
+    if (s < kt_total) issue(s, s >= kt_full);
+  if (kt_total > 0) {
+    wait_stages<LPS>(min(kStages, kt_total) - 1);
+    lds_barrier();
+    if (kfix && kt_full == 0) {
+      zero_k_padding(0);
+      lds_barrier();
     }
+    read_frags(0, fa0, fb0);
+  }
+
+  // Steady state, two stages per trip with no conditions: make stage kt+1
+  // visible, refill the buffer stage kt freed with stage kt+kStages, read
+  // stage kt+1's fragments, run stage kt's MFMAs.
+  auto steady = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
+                    __attribute__((always_inline)) {
+    wait_stages<LPS>(kStages - 2);
+    lds_barrier();
+    issue(kt + kStages, kt + kStages >= kt_full);
+    read_frags(kt + 1, na, nb);
+    mfmas(fa, fb);
+  };
+  // The last stages: the same with the prefetch and the next reads guarded.
+  auto drain = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
+                   __attribute__((always_inline)) {
+    if (kt + 1 < kt_total) {
+      wait_stages<LPS>(min(kt + kStages - 1, kt_total - 1) - (kt + 1));
+      lds_barrier();
+      if (kfix && kt + 1 == kt_full) {
+        zero_k_padding(kt + 1);
+        lds_barrier();
+      }
+      if (kt + kStages < kt_total) issue(kt + kStages, kt + kStages >= kt_full);
+      read_frags(kt + 1, na, nb);
+    }
+    mfmas(fa, fb);
+  };
+  int kt = 0;
+  for (; kt + kStages + 1 < kt_total; kt += 2) {
+    steady(kt, fa0, fb0, fa1, fb1);
+    steady(kt + 1, fa1, fb1, fa0, fb0);
+  }
+  for (; kt < kt_total; kt += 2) {
+    drain(kt, fa0, fb0, fa1, fb1);
+    if (kt + 1 < kt_total) drain(kt + 1, fa1, fb1, fa0, fb0);
   }
 
   // Epilogue: y = acc * (sa_inv * sb_inv) + bias[n], one bf16 rounding.

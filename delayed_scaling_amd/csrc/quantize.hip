@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kQBlock = 256;     // threads per block
 constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
+constexpr int kDefaultBlocks = 2048;  // grid cap: 8 blocks per CU; larger inputs loop
 
 // Casts two products to the format's codes in the low or high half-word of
 // `word`.  Products are clamped to +-FMAX first because the hardware convert
@@ -145,15 +146,22 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
 
   const uint32_t bmax = block_max(amax16, red) << 16;   // |x| as fp32 bits
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    // Both words are device-scope atomics on one cache line, performed where
+    // all XCDs see them.  The ticket is taken only after the max has been
+    // performed (its returned value is waited for), so whoever draws the last
+    // ticket reads a maximum that includes every block.  No release/acquire
+    // fence is needed: nothing else this block wrote is read by the last
+    // block, and an agent-scope fence would write back the whole L2.
+    const uint32_t prev = __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" : : "v"(prev) : "memory");
+    const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (t == gridDim.x - 1);
   }
   __syncthreads();
   if (!s_last) return;
 
   // Last block: fold, reduce the window, publish.
-  const uint32_t a = __hip_atomic_load(&ring->amax_bits, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t a = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int H = ring->hist_len;
   const int idx = ring->idx;
   const bool bad_header = H < 1 || H > 1024 || idx < 0 || idx >= H;
@@ -216,6 +224,7 @@ int launch_quantize(const void* x, int64_t numel, int fmt, void* ring, void* y, 
   const int64_t per_block = (int64_t)kQBlock * kQUnroll;
   int64_t blocks = (nchunk + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
+  if (max_blocks <= 0) max_blocks = kDefaultBlocks;
   if (blocks > max_blocks) blocks = max_blocks;
   const v4u* xv = static_cast<const v4u*>(x);
   v2u* yv = static_cast<v2u*>(y);

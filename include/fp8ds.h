@@ -109,6 +109,11 @@ int scale_ring_init(void* ring, int hist_len, int fmt, float init_scale, void* s
  * ring == NULL (dynamic scaling) returns FP8DS_EUNSUPPORTED. */
 int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, void* stream);
 
+/* fp8_quantize with the grid capped at max_blocks workgroups of 256 threads
+ * (0 = the default cap); same results bit for bit, for tuning sweeps. */
+int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, int max_blocks,
+                           void* stream);
+
 /* Scaled FP8 GEMM arguments.  Zero-initialise and set what you use: a
  * zeroed field means "absent" (gemm.cuh history @5e76fbd1, null-default
  * params entry). */
