@@ -24,6 +24,8 @@ E5M2 = 1
 NT, NN, TN = 0, 1, 2
 BIAS_NONE, BIAS_BF16, BIAS_F32 = 0, 1, 2
 TILES = {"256x256": 0, "128x128": 1, "64x64": 2}
+RING_HIST_OFFSET = 2112   # byte offset of hist[] in a ring (include/fp8ds.h)
+RING_GROUPS = 32          # completion-tree scratch lines after the 64-byte header
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp8ds.so")
@@ -122,11 +124,13 @@ def read_ring(buf):
     """Copy a ring to the host and decode its fields (layout of include/fp8ds.h)."""
     raw = buf.detach().cpu().numpy().tobytes()
     scale, sinv, amax_last, idx, hist_len, fmt, status, _r0, amax_bits, ticket = struct.unpack_from("<fffiiiIIII", raw, 0)
-    hist = list(struct.unpack_from(f"<{hist_len}f", raw, 64)) if 1 <= hist_len <= 1024 else []
-    hist_bits = list(struct.unpack_from(f"<{hist_len}I", raw, 64)) if 1 <= hist_len <= 1024 else []
+    hist = list(struct.unpack_from(f"<{hist_len}f", raw, RING_HIST_OFFSET)) if 1 <= hist_len <= 1024 else []
+    hist_bits = list(struct.unpack_from(f"<{hist_len}I", raw, RING_HIST_OFFSET)) if 1 <= hist_len <= 1024 else []
+    groups = struct.unpack_from("<" + "II56x" * RING_GROUPS, raw, 64)
     return {"scale": scale, "scale_inv_used": sinv, "amax_last": amax_last, "idx": idx,
             "hist_len": hist_len, "fmt": fmt, "status": status, "amax_bits": amax_bits,
             "ticket": ticket, "hist": hist, "hist_bits": hist_bits,
+            "group_scratch_zero": all(v == 0 for v in groups),
             "scale_bits": struct.unpack_from("<I", raw, 0)[0],
             "scale_inv_used_bits": struct.unpack_from("<I", raw, 4)[0],
             "amax_last_bits": struct.unpack_from("<I", raw, 8)[0]}

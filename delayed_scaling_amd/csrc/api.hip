@@ -52,7 +52,7 @@ const char* fp8_last_error(void) { return g_err; }
 
 size_t fp8_scale_ring_bytes(int hist_len) {
   if (hist_len < 1 || hist_len > FP8DS_RING_MAX_HIST) return 0;
-  return (size_t)FP8DS_RING_HEADER_BYTES + (((size_t)hist_len * 4 + 15) & ~(size_t)15);
+  return (size_t)FP8DS_RING_HIST_OFFSET + (((size_t)hist_len * 4 + 15) & ~(size_t)15);
 }
 
 const float* fp8_ring_scale_inv(const void* ring) {

@@ -36,6 +36,23 @@ struct RingHeader {
 };
 static_assert(sizeof(RingHeader) == 64, "ring header is 64 bytes");
 
+// Completion-tree scratch of the ring: one 64-byte line per block group, so
+// the per-block atomics of a quantize launch spread over kRingGroups lines
+// instead of queueing on one address.  Zero between calls.
+constexpr int kRingGroups = 32;
+struct RingGroup {
+  uint32_t amax_bits;
+  uint32_t ticket;
+  uint32_t pad[14];
+};
+static_assert(sizeof(RingGroup) == 64, "one group per 64-byte line");
+constexpr int kRingHistOffset = 64 + kRingGroups * 64;   // 2112
+
+__device__ __forceinline__ RingGroup* ring_groups(RingHeader* r) { return reinterpret_cast<RingGroup*>(r + 1); }
+__device__ __forceinline__ float* ring_hist(RingHeader* r) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(r) + kRingHistOffset);
+}
+
 constexpr uint32_t kStatusFmtMismatch = 1u;
 constexpr uint32_t kStatusBadHeader = 2u;
 

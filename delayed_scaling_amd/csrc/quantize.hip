@@ -6,9 +6,10 @@
 //
 // One launch streams x once (16-byte loads, 8-byte stores), so the kernel is
 // bound by HBM: 3 bytes per element.  Each block reduces max|x| over its
-// elements, publishes it with one device-scope atomic max, and takes a ticket;
-// the block holding the last ticket finalizes the ring and resets the two
-// scratch words for the next call on the same stream.
+// elements and climbs a two-level completion tree kept in the ring's scratch
+// lines (per-group max + ticket, then a top-level max + ticket); the block
+// holding the last top-level ticket finalizes the ring and every scratch
+// word is back at zero for the next call on the same stream.
 #include "device_common.h"
 #include "launch.h"
 
@@ -18,7 +19,7 @@ namespace {
 
 constexpr int kQBlock = 256;     // threads per block
 constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
-constexpr int kDefaultBlocks = 2048;  // grid cap: 8 blocks per CU; larger inputs loop
+constexpr int kDefaultBlocks = 1024;  // grid cap: 4 blocks per CU; larger inputs loop
 
 // Casts two products to the format's codes in the low or high half-word of
 // `word`.  Products are clamped to +-FMAX first because the hardware convert
@@ -78,6 +79,14 @@ __device__ __forceinline__ void quant_chunk(v4u v, float scale, v2u& out, uint32
     out.x = fix_nan4(v.x, v.y, out.x);
     out.y = fix_nan4(v.z, v.w, out.y);
   }
+}
+
+// Waits until every vector-memory operation of this wave has completed,
+// the returning atomic that produced v included, before anything after it
+// is issued.  The completion tree orders its atomics this way rather than by
+// release/acquire fences (an agent-scope fence writes back the whole L2).
+__device__ __forceinline__ void wait_returned(uint32_t v) {
+  asm volatile("s_waitcnt vmcnt(0)" : : "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
@@ -146,27 +155,55 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
 
   const uint32_t bmax = block_max(amax16, red) << 16;   // |x| as fp32 bits
   if (threadIdx.x == 0) {
-    // Both words are device-scope atomics on one cache line, performed where
-    // all XCDs see them.  The ticket is taken only after the max has been
-    // performed (its returned value is waited for), so whoever draws the last
-    // ticket reads a maximum that includes every block.  No release/acquire
-    // fence is needed: nothing else this block wrote is read by the last
-    // block, and an agent-scope fence would write back the whole L2.
-    const uint32_t prev = __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" : : "v"(prev) : "memory");
-    const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (t == gridDim.x - 1);
+    // Two-level completion tree.  Block b belongs to group b % kRingGroups;
+    // each group has its own cache line holding a running max and a ticket.
+    // All words are device-scope atomics, performed where every XCD sees
+    // them.  A ticket is taken only after the max it covers has been
+    // performed (its returned value is waited for), so the block drawing a
+    // group's last ticket reads a max that covers the whole group, and the
+    // block drawing the last top-level ticket reads the max of all groups.
+    // No release/acquire fence is needed: nothing else a block wrote is read
+    // by the finalizing block, and an agent-scope fence would write back the
+    // whole L2.
+    const int G = (int)gridDim.x;
+    const int ngroups = G < kRingGroups ? G : kRingGroups;
+    const int g = (int)blockIdx.x % kRingGroups;
+    const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);
+    RingGroup* grp = ring_groups(ring) + g;
+    const uint32_t prev = __hip_atomic_fetch_max(&grp->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(prev);
+    const uint32_t t = __hip_atomic_fetch_add(&grp->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(t);
+    int last = 0;
+    if (t == members - 1) {
+      // Every member has performed its max and taken its ticket, so this
+      // block alone touches the group line now: read it, then clear it.
+      // (Plain atomic loads and stores: an exchange whose returned value
+      // shared a register with its data was measured returning the new value
+      // on this target.)
+      const uint32_t gmax = __hip_atomic_load(&grp->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_returned(gmax);
+      __hip_atomic_store(&grp->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&grp->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t prev2 = __hip_atomic_fetch_max(&ring->amax_bits, gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_returned(prev2);
+      const uint32_t t2 = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_returned(t2);
+      last = t2 == (uint32_t)ngroups - 1;
+    }
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
 
   // Last block: fold, reduce the window, publish.
   const uint32_t a = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(a);
   const int H = ring->hist_len;
   const int idx = ring->idx;
   const bool bad_header = H < 1 || H > 1024 || idx < 0 || idx >= H;
   const bool fmt_mismatch = ring->fmt != FMT;
-  float* hist = reinterpret_cast<float*>(ring + 1);
+  float* hist = ring_hist(ring);
   uint32_t w = 0;
   if (!bad_header) {
     for (int j = threadIdx.x; j < H; j += kQBlock) w = max(w, j == idx ? a : __float_as_uint(hist[j]));
@@ -193,8 +230,10 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
 }
 
 __global__ __launch_bounds__(256) void ring_init_kernel(RingHeader* ring, int hist_len, int fmt, float init_scale) {
-  float* hist = reinterpret_cast<float*>(ring + 1);
+  float* hist = ring_hist(ring);
   for (int j = threadIdx.x; j < hist_len; j += blockDim.x) hist[j] = 0.0f;
+  uint32_t* scratch = reinterpret_cast<uint32_t*>(ring_groups(ring));
+  for (int j = threadIdx.x; j < kRingGroups * 16; j += blockDim.x) scratch[j] = 0u;
   if (threadIdx.x == 0) {
     ring->scale = init_scale;
     ring->scale_inv_used = 1.0f / init_scale;

@@ -65,9 +65,11 @@ enum {
  *   24      uint32   status          sticky device-side error bits (see below)
  *   28      uint32   (reserved, 0)
  *   32      uint32   amax_bits       scratch: running max of |x| bits, 0 between calls
- *   36      uint32   ticket          scratch: finished-block counter, 0 between calls
+ *   36      uint32   ticket          scratch: finished-group counter, 0 between calls
  *   40..63           (reserved, 0)
- *   64      float    hist[H]         amax history window
+ *   64      32 x 64 B                scratch: per block-group {uint32 amax_bits,
+ *                                    uint32 ticket, 56 B pad}, 0 between calls
+ *   2112    float    hist[H]         amax history window
  *
  * The ring is the only state of the method: copying its bytes out and back
  * checkpoints and restores it.  Calls that use one ring must be ordered on
@@ -78,10 +80,11 @@ enum {
  * unchanged; its output bytes are unspecified.
  * ------------------------------------------------------------------------- */
 #define FP8DS_RING_HEADER_BYTES 64
+#define FP8DS_RING_HIST_OFFSET 2112
 #define FP8DS_RING_MAX_HIST 1024
 
-/* Bytes of a ring with hist_len slots (rounded up to 16); 0 if hist_len is
- * outside [1, 1024]. */
+/* Bytes of a ring with hist_len slots: 2112 + 4 * hist_len rounded up to 16;
+ * 0 if hist_len is outside [1, 1024]. */
 size_t fp8_scale_ring_bytes(int hist_len);
 
 /* Device address of a ring's scale_inv_used field (ring + 4), for

@@ -43,10 +43,10 @@ def test_library_exports_every_declared_function(L):
 def test_ring_bytes(L):
     assert ds.scale_ring_bytes(0) == 0
     assert ds.scale_ring_bytes(1025) == 0
-    assert ds.scale_ring_bytes(1) == 64 + 16
-    assert ds.scale_ring_bytes(4) == 64 + 16
-    assert ds.scale_ring_bytes(16) == 64 + 64
-    assert ds.scale_ring_bytes(1024) == 64 + 4096
+    assert ds.scale_ring_bytes(1) == 2112 + 16
+    assert ds.scale_ring_bytes(4) == 2112 + 16
+    assert ds.scale_ring_bytes(16) == 2112 + 64
+    assert ds.scale_ring_bytes(1024) == 2112 + 4096
     assert L.fp8_ring_scale_inv(ctypes.c_void_p(4096)) == 4100
 
 

@@ -20,6 +20,7 @@ def assert_ring_equal(gpu, ref, where=""):
     assert gpu["idx"] == ref.idx, where
     assert gpu["hist_bits"] == [int(v) for v in ref.hist.view(np.uint32)], where
     assert gpu["amax_bits"] == 0 and gpu["ticket"] == 0 and gpu["status"] == 0, where
+    assert gpu["group_scratch_zero"], where
 
 
 def run_steps(ds, xs, fmt, hist_len, init_scale=1.0):
