@@ -204,22 +204,39 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   for (int j = 0; j < B_LOADS; ++j)
     b_voff[j] = slot_offset<B_KC, BN>((j * 4 + wave) * 64 + lane, n0, p.n, p.ldb, b_kpos[j]);
 
-  // Global -> LDS loads of K stage kt into LDS buffer kt % kStages.
-  auto issue = [&](int kt, bool tail) __attribute__((always_inline)) {
+  // Global -> LDS loads of K stage kt into LDS buffer kt % kStages: the
+  // scalar part (descriptors, LDS bases) once per stage, then one
+  // buffer_load ... lds per call of issue_one.
+  struct LoadCtx {
+    v4i ra, rb;
+    uint32_t la, lb;
+    int klim;
+    bool tail;
+  };
+  auto load_ctx = [&](int kt, bool tail) __attribute__((always_inline)) {
     const int k0 = kt * kBK;
-    const int klim = p.k - k0;
     const uint32_t a_adv = A_KC ? (uint32_t)k0 : (uint32_t)k0 * p.lda;
     const uint32_t b_adv = B_KC ? (uint32_t)k0 : (uint32_t)k0 * p.ldb;
-    const v4i ra = rsrc_words(a_tile + a_adv, a_rem > a_adv ? a_rem - a_adv : 0u);
-    const v4i rb = rsrc_words(b_tile + b_adv, b_rem > b_adv ? b_rem - b_adv : 0u);
-    const uint32_t la = lds_address(smem + (kt % kStages) * STAGE) + wave * 1024;
-    const uint32_t lb = la + A_BYTES;
+    LoadCtx c;
+    c.ra = rsrc_words(a_tile + a_adv, a_rem > a_adv ? a_rem - a_adv : 0u);
+    c.rb = rsrc_words(b_tile + b_adv, b_rem > b_adv ? b_rem - b_adv : 0u);
+    c.la = lds_address(smem + (kt % kStages) * STAGE) + wave * 1024;
+    c.lb = c.la + A_BYTES;
+    c.klim = p.k - k0;
+    c.tail = tail;
+    return c;
+  };
+  auto issue_one = [&](const LoadCtx& c, int j) __attribute__((always_inline)) {
+    if (j < A_LOADS)
+      load_lds16(c.ra, c.la + j * 4096, (c.tail && a_kpos[j] >= c.klim) ? kOOB : a_voff[j]);
+    else
+      load_lds16(c.rb, c.lb + (j - A_LOADS) * 4096,
+                 (c.tail && b_kpos[j - A_LOADS] >= c.klim) ? kOOB : b_voff[j - A_LOADS]);
+  };
+  auto issue = [&](int kt, bool tail) __attribute__((always_inline)) {
+    const LoadCtx c = load_ctx(kt, tail);
 #pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
-      load_lds16(ra, la + j * 4096, (tail && a_kpos[j] >= klim) ? kOOB : a_voff[j]);
-#pragma unroll
-    for (int j = 0; j < B_LOADS; ++j)
-      load_lds16(rb, lb + j * 4096, (tail && b_kpos[j] >= klim) ? kOOB : b_voff[j]);
+    for (int j = 0; j < LPS; ++j) issue_one(c, j);
   };
 
   // The chunk holding K's last bytes also holds the row's padding; zero the
@@ -282,15 +299,35 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   }
 
   // Steady state, two stages per trip with no conditions: make stage kt+1
-  // visible, refill the buffer stage kt freed with stage kt+kStages, read
-  // stage kt+1's fragments, run stage kt's MFMAs.
+  // visible, then issue stage kt's MFMAs one by one, each followed by its
+  // share of the global loads of stage kt+kStages (into the buffer stage kt
+  // freed) and of the LDS reads of stage kt+1's fragments.  Scheduling
+  // barriers keep that interleave: bursts of loads or LDS reads right after
+  // the barrier left the matrix cores idle.  The wave runs at raised priority
+  // while it issues the MFMA stream.
+  constexpr int NM = TM * TN, NF = TM + TN;
   auto steady = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
                     __attribute__((always_inline)) {
     wait_stages<LPS>(kStages - 2);
     lds_barrier();
-    issue(kt + kStages, kt + kStages >= kt_full);
-    read_frags(kt + 1, na, nb);
-    mfmas(fa, fb);
+    const LoadCtx c = load_ctx(kt + kStages, kt + kStages >= kt_full);
+    const lds_char_t* sa = smem + ((kt + 1) % kStages) * STAGE;
+    const lds_char_t* sb = sa + A_BYTES;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int i = q / TM, j = q % TM;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+#pragma unroll
+      for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) issue_one(c, l);
+#pragma unroll
+      for (int f = q * NF / NM; f < (q + 1) * NF / NM; ++f) {
+        if (f < TM) na[f] = load_frag<A_KC, BM>(sa, wm * WM + f * 32, lane);
+        else nb[f - TM] = load_frag<B_KC, BN>(sb, wn * WN + (f - TM) * 32, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
   // The last stages: the same with the prefetch and the next reads guarded.
   auto drain = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
