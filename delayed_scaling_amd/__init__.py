@@ -23,7 +23,7 @@ E4M3 = 0
 E5M2 = 1
 NT, NN, TN = 0, 1, 2
 BIAS_NONE, BIAS_BF16, BIAS_F32 = 0, 1, 2
-TILES = {"256x256": 0, "128x128": 1, "64x64": 2}
+TILES = {"256x256": 0, "128x128": 1, "64x64": 2, "256x128": 3, "128x256": 4, "256x256w8n": 5, "256x256w8": 6}
 RING_HIST_OFFSET = 2112   # byte offset of hist[] in a ring (include/fp8ds.h)
 RING_GROUPS = 32          # completion-tree scratch lines after the 64-byte header
 

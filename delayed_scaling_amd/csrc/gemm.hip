@@ -35,8 +35,6 @@ namespace fp8ds {
 namespace {
 
 constexpr int kBK = 64;           // K bytes (= elements) per pipeline stage
-constexpr int kStages = 4;        // LDS stages in flight
-constexpr int kThreads = 256;     // 4 waves
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every buffer: loads give zero
 
 struct GemmKArgs {
@@ -153,9 +151,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Wait until at most `stages` stages of LPS loads each are still in flight.
-template <int LPS>
+template <int LPS, int STAGES>
 __device__ __forceinline__ void wait_stages(int stages) {
-  static_assert(LPS * (kStages - 1) <= 63, "vmcnt holds at most 63");
+  static_assert(LPS * (STAGES - 1) <= 63, "vmcnt holds at most 63");
   if (stages >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPS));
   else if (stages == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
   else if (stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
@@ -170,12 +168,13 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int FA, int FB, int OCC>
-__global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int WGM, int WGN, int kStages, bool A_KC, bool B_KC, int FA, int FB, int OCC>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
+  constexpr int NW = WGM * WGN, kThreads = 64 * NW;   // waves in a WGM x WGN grid
+  constexpr int WM = BM / WGM, WN = BN / WGN;          // C block of one wave
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = A_BYTES / 1024 / 4, B_LOADS = B_BYTES / 1024 / 4;
+  constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;
   constexpr int LPS = A_LOADS + B_LOADS;
   static_assert(TM >= 1 && TN >= 1 && A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
   __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * STAGE];
@@ -183,7 +182,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WGM, wn = wave / WGM;
   int bt, tmi, tni;
   map_tile(p, bt, tmi, tni);
   const int m0 = tmi * BM, n0 = tni * BN;
@@ -199,10 +198,10 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   int a_kpos[A_LOADS], b_kpos[B_LOADS];
 #pragma unroll
   for (int j = 0; j < A_LOADS; ++j)
-    a_voff[j] = slot_offset<A_KC, BM>((j * 4 + wave) * 64 + lane, m0, p.m, p.lda, a_kpos[j]);
+    a_voff[j] = slot_offset<A_KC, BM>((j * NW + wave) * 64 + lane, m0, p.m, p.lda, a_kpos[j]);
 #pragma unroll
   for (int j = 0; j < B_LOADS; ++j)
-    b_voff[j] = slot_offset<B_KC, BN>((j * 4 + wave) * 64 + lane, n0, p.n, p.ldb, b_kpos[j]);
+    b_voff[j] = slot_offset<B_KC, BN>((j * NW + wave) * 64 + lane, n0, p.n, p.ldb, b_kpos[j]);
 
   // Global -> LDS loads of K stage kt into LDS buffer kt % kStages: the
   // scalar part (descriptors, LDS bases) once per stage, then one
@@ -228,9 +227,9 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   };
   auto issue_one = [&](const LoadCtx& c, int j) __attribute__((always_inline)) {
     if (j < A_LOADS)
-      load_lds16(c.ra, c.la + j * 4096, (c.tail && a_kpos[j] >= c.klim) ? kOOB : a_voff[j]);
+      load_lds16(c.ra, c.la + j * NW * 1024, (c.tail && a_kpos[j] >= c.klim) ? kOOB : a_voff[j]);
     else
-      load_lds16(c.rb, c.lb + (j - A_LOADS) * 4096,
+      load_lds16(c.rb, c.lb + (j - A_LOADS) * NW * 1024,
                  (c.tail && b_kpos[j - A_LOADS] >= c.klim) ? kOOB : b_voff[j - A_LOADS]);
   };
   auto issue = [&](int kt, bool tail) __attribute__((always_inline)) {
@@ -289,7 +288,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   for (int s = 0; s < kStages; ++s)
     if (s < kt_total) issue(s, s >= kt_full);
   if (kt_total > 0) {
-    wait_stages<LPS>(min(kStages, kt_total) - 1);
+    wait_stages<LPS, kStages>(min(kStages, kt_total) - 1);
     lds_barrier();
     if (kfix && kt_full == 0) {
       zero_k_padding(0);
@@ -308,7 +307,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   constexpr int NM = TM * TN, NF = TM + TN;
   auto steady = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
                     __attribute__((always_inline)) {
-    wait_stages<LPS>(kStages - 2);
+    wait_stages<LPS, kStages>(kStages - 2);
     lds_barrier();
     const LoadCtx c = load_ctx(kt + kStages, kt + kStages >= kt_full);
     const lds_char_t* sa = smem + ((kt + 1) % kStages) * STAGE;
@@ -333,7 +332,7 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
   auto drain = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
                    __attribute__((always_inline)) {
     if (kt + 1 < kt_total) {
-      wait_stages<LPS>(min(kt + kStages - 1, kt_total - 1) - (kt + 1));
+      wait_stages<LPS, kStages>(min(kt + kStages - 1, kt_total - 1) - (kt + 1));
       lds_barrier();
       if (kfix && kt + 1 == kt_full) {
         zero_k_padding(kt + 1);
@@ -413,20 +412,27 @@ __global__ __launch_bounds__(kThreads, OCC) void gemm_kernel(GemmKArgs p) {
 // Host side: tile family and dispatch.
 
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, waves;
 };
-constexpr TileCfg kTiles[] = {{256, 256}, {128, 128}, {64, 64}};
+// Tile family (index = the tile argument of fp8_mm_with_tile).  256x256 with
+// four waves runs one workgroup per CU (4 LDS stages, 128 KiB), each wave a
+// 128x128 block; the eight-wave 256x256 tiles give every SIMD two waves of a
+// 128x64 / 64x128 block so one wave's memory stalls hide behind the other's
+// MFMAs; 256x128 / 128x256 run two workgroups per CU (3 stages, 72 KiB
+// each); 128x128 and 64x64 serve problems too small to fill the chip.
+constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
+                              {128, 256, 4}, {256, 256, 8}, {256, 256, 8}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 typedef void (*GemmFn)(GemmKArgs);
 
-template <int BM, int BN, int OCC>
+template <int BM, int BN, int WGM, int WGN, int ST, int OCC>
 GemmFn pick_kernel(int layout, int fa, int fb) {
-#define FP8DS_FMT_CASES(AKC, BKC)                                                     \
-  if (fa == 0 && fb == 0) return gemm_kernel<BM, BN, AKC, BKC, 0, 0, OCC>;            \
-  if (fa == 1 && fb == 0) return gemm_kernel<BM, BN, AKC, BKC, 1, 0, OCC>;            \
-  if (fa == 0 && fb == 1) return gemm_kernel<BM, BN, AKC, BKC, 0, 1, OCC>;            \
-  return gemm_kernel<BM, BN, AKC, BKC, 1, 1, OCC>;
+#define FP8DS_FMT_CASES(AKC, BKC)                                                              \
+  if (fa == 0 && fb == 0) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 0, 0, OCC>;       \
+  if (fa == 1 && fb == 0) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 1, 0, OCC>;       \
+  if (fa == 0 && fb == 1) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 0, 1, OCC>;       \
+  return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 1, 1, OCC>;
   if (layout == 0) { FP8DS_FMT_CASES(true, true) }
   if (layout == 1) { FP8DS_FMT_CASES(true, false) }
   FP8DS_FMT_CASES(false, false)
@@ -435,9 +441,13 @@ GemmFn pick_kernel(int layout, int fa, int fb) {
 
 GemmFn kernel_for(int tile, int layout, int fa, int fb) {
   switch (tile) {
-    case 0: return pick_kernel<256, 256, 1>(layout, fa, fb);
-    case 1: return pick_kernel<128, 128, 2>(layout, fa, fb);
-    default: return pick_kernel<64, 64, 4>(layout, fa, fb);
+    case 0: return pick_kernel<256, 256, 2, 2, 4, 1>(layout, fa, fb);
+    case 1: return pick_kernel<128, 128, 2, 2, 4, 2>(layout, fa, fb);
+    case 2: return pick_kernel<64, 64, 2, 2, 4, 4>(layout, fa, fb);
+    case 3: return pick_kernel<256, 128, 2, 2, 3, 2>(layout, fa, fb);
+    case 4: return pick_kernel<128, 256, 2, 2, 3, 2>(layout, fa, fb);
+    case 5: return pick_kernel<256, 256, 2, 4, 4, 1>(layout, fa, fb);
+    default: return pick_kernel<256, 256, 4, 2, 4, 1>(layout, fa, fb);
   }
 }
 
@@ -445,12 +455,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Largest tile whose grid still fills the 256 CUs; else the one with most tiles.
 int choose_tile(const GemmProblem& p) {
+  // Largest tile whose grid still fills the 256 CUs, else the one with most
+  // tiles.  For the 256x256 size the eight-wave variant measured faster.
   constexpr int64_t kCUs = 256;
-  for (int t = 0; t < kNumTiles; ++t) {
+  constexpr int order[] = {6, 1, 2};
+  for (int t : order) {
     const int64_t tiles = cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch;
     if (tiles >= kCUs) return t;
   }
-  return kNumTiles - 1;
+  return 2;
 }
 
 }  // namespace
@@ -483,7 +496,7 @@ int launch_gemm(const GemmProblem& p, int tile_override, hipStream_t stream) {
   const int64_t total = (int64_t)k.tiles_m * k.tiles_n * k.batch;
   if (total > 0x7FFFFFFF) return set_error(-3, "fp8_mm: %lld tiles exceed the grid limit", (long long)total);
   GemmFn fn = kernel_for(t, p.layout, p.fmt_a, p.fmt_b);
-  hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(kThreads), 0, stream, k);
+  hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(64 * kTiles[t].waves), 0, stream, k);
   return check_launch("gemm_kernel");
 }
 

@@ -149,7 +149,8 @@ typedef struct fp8_mm_args {
 int fp8_mm(const fp8_mm_args* args, void* stream);
 
 /* fp8_mm with the workgroup tile forced: tile = index into the tile family
- * (0: 256x256, 1: 128x128, 2: 64x64), -1 = the automatic choice.  Same
+ * (M x N: 0: 256x256, 1: 128x128, 2: 64x64, 3: 256x128, 4: 128x256, 5 and 6:
+ * 256x256 with eight waves), -1 = the automatic choice.  Same
  * results within the tolerance of fp8_mm; for tests and tuning sweeps. */
 int fp8_mm_with_tile(const fp8_mm_args* args, int tile, void* stream);
 
