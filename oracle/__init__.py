@@ -14,13 +14,13 @@ library casts and brute force; none is "parity unpinned".
 """
 from .formats import (E4M3, E5M2, FMAX, bf16_to_f32, bf16_ulp, decode_fp8,
                       encode_fp8, f64_to_bf16)
-from .scaling import (Ring, amax, next_scale, quantize_step, quantize_values,
+from .scaling import (Ring, advance_ring, amax, next_scale, quantize_step, quantize_values,
                       ring_init)
 from .gemm import NN, NT, TN, max_abs_dequant, mm, mm_entries, operand_matrices, tolerance
 
 __all__ = [
     "E4M3", "E5M2", "FMAX", "bf16_to_f32", "bf16_ulp", "decode_fp8", "encode_fp8",
-    "f64_to_bf16", "Ring", "amax", "next_scale", "quantize_step", "quantize_values",
+    "f64_to_bf16", "Ring", "advance_ring", "amax", "next_scale", "quantize_step", "quantize_values",
     "ring_init", "NT", "NN", "TN", "mm", "mm_entries", "operand_matrices", "tolerance",
     "max_abs_dequant",
 ]

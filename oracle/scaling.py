@@ -97,27 +97,32 @@ def next_scale(hist, fmt, old_scale):
     return t if np.isfinite(t) else np.float32(old_scale)
 
 
-def quantize_step(ring, x_bf16):
-    """One delayed-scaling quantize call.
-
-    Returns (codes, new ring).  In order: quantize with the current scale;
-    fold amax into hist[idx] and advance idx; publish the next scale from the
-    window; record 1/scale_used and the amax.
-    """
-    x = np.asarray(x_bf16, dtype=np.uint16)
+def advance_ring(ring, a):
+    """The ring update of one quantize call whose tensor had amax `a`:
+    fold a into hist[idx] and advance idx; publish the next scale from the
+    window; record 1/scale_used and the amax.  Returns the new ring."""
     r = ring.copy()
-    if x.size == 0:
-        return np.zeros(x.shape, dtype=np.uint8), r
     s_used = np.float32(r.scale)
-    codes = quantize_values(x, s_used, r.fmt)
-    a = amax(x)
-    r.hist[r.idx] = a
+    r.hist[r.idx] = np.float32(a)
     r.idx = (r.idx + 1) % r.hist_len
     r.scale = next_scale(r.hist, r.fmt, s_used)
     r.scale_inv_used = np.float32(1.0) / s_used
-    r.amax_last = a
-    return codes, r
+    r.amax_last = np.float32(a)
+    return r
 
 
-__all__ = ["Ring", "ring_init", "amax", "quantize_values", "next_scale",
+def quantize_step(ring, x_bf16):
+    """One delayed-scaling quantize call.
+
+    Returns (codes, new ring).  In order: quantize with the current scale,
+    then advance the ring with the tensor's amax (advance_ring).
+    """
+    x = np.asarray(x_bf16, dtype=np.uint16)
+    if x.size == 0:
+        return np.zeros(x.shape, dtype=np.uint8), ring.copy()
+    codes = quantize_values(x, np.float32(ring.scale), ring.fmt)
+    return codes, advance_ring(ring, amax(x))
+
+
+__all__ = ["Ring", "ring_init", "amax", "quantize_values", "next_scale", "advance_ring",
            "quantize_step", "E4M3", "E5M2", "FMAX"]
