@@ -36,6 +36,17 @@ def bf16_normal(shape, seed, sigma=1.0, outliers=False):
     return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def bf16_normal_sequence(shapes, seed, sigma=1.0):
+    """Several bf16 tensors drawn one after another from one CPU generator
+    seeded with `seed` (the tiny workload draws X, W and bias this way)."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    out = []
+    for shape in shapes:
+        x = torch.randn(tuple(shape), generator=g, dtype=torch.float32) * float(sigma)
+        out.append(x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    return out
+
+
 def bf16_from_float(values):
     """bf16 bit patterns of given float values (nearest-even), for hand-made
     small inputs."""
