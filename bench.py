@@ -35,8 +35,8 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--size", type=int, default=8192, help="M = N = K of the square workload")
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
@@ -44,16 +44,16 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per GEMM launch recorded in profiles/ by the two PMC runs,
-    or None when the kernel source changed since they were taken."""
+def traffic_from_profile(kernel_src, sha_key, bytes_key):
+    """HBM bytes per launch recorded in profiles/ by the two PMC runs, or
+    None when the kernel source changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_sha = re.search(rf"^{sha_key}:\s*([0-9a-f]{{64}})", text, re.M)
+    m_b = re.search(rf"^{bytes_key}:\s*([0-9.eE+]+)", text, re.M)
     if not m_sha or not m_b or m_sha.group(1) != sha:
         return None
     return float(m_b.group(1))
@@ -156,7 +156,10 @@ def main():
     q_bytes = 3.0 * n * n
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip"))
+    traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip"),
+                                   "kernel_source_sha256", "hbm_bytes_per_launch")
+    q_traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip"),
+                                     "quantize_source_sha256", "quantize_hbm_bytes_per_launch")
 
     out = {
         "metric": "FP8 GEMM TFLOP/s (E4M3 NT 8192^3) + quantize GB/s, % of MI355X peak",
@@ -176,11 +179,12 @@ def main():
                    "m": n, "n": n, "k": n, "hist_len": 16, "input_rotation": rot},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm_kernel<256,256,NT,E4M3,E4M3>",
+                     "traffic": traffic, "kernel": "gemm_kernel 256x256 tile, 8 waves, NT, E4M3 x E4M3",
                      "avg_launch_us": round(g_avg * 1e3, 2)},
         "roofline_quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                               "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
-                              "kernel": "quantize_kernel<E4M3>", "bytes_per_launch": q_bytes,
+                              "traffic": q_traffic, "kernel": "quantize_kernel<E4M3>",
+                              "bytes_per_launch": q_bytes,
                               "avg_launch_us": round(q_avg * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
