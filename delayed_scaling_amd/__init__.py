@@ -71,6 +71,8 @@ def lib():
         L.fp8_mm.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_void_p]
         L.fp8_mm_with_tile.restype = ctypes.c_int
         L.fp8_mm_with_tile.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_void_p]
+        L.fp8_mm_with_grid.restype = ctypes.c_int
+        L.fp8_mm_with_grid.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.fp8_last_error.restype = ctypes.c_char_p
         L.fp8_last_error.argtypes = []
         _lib = L
@@ -163,13 +165,15 @@ def _addr(x):
 
 def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
            batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
-           tile=None, stream=None):
+           tile=None, max_workgroups=None, stream=None):
     """C = bf16(A @ B * a_scale_inv * b_scale_inv + bias) on uint8 fp8 code tensors.
 
     a, b: uint8 device tensors holding the stored operands (see include/fp8ds.h
     for the NT/NN/TN storage); a_scale_inv / b_scale_inv: ScaleRing, fp32 device
     tensor or device address; bias: bf16 or fp32 device tensor [n] or None.
     Leading dimensions and batch strides default to the dense layout.
+    tile forces a tile of the family (TILES name or index); max_workgroups
+    bounds the grid so each workgroup runs several output tiles.
     """
     a_cols = m if layout == TN else k
     b_cols = k if layout == NT else n
@@ -193,11 +197,11 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
                    int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
                    int(stride_a), int(stride_b), int(stride_c),
                    _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias))
-    if tile is None:
+    if tile is None and max_workgroups is None:
         _check(lib().fp8_mm(ctypes.byref(args), _stream(stream)))
     else:
-        t = TILES[tile] if isinstance(tile, str) else int(tile)
-        _check(lib().fp8_mm_with_tile(ctypes.byref(args), t, _stream(stream)))
+        t = -1 if tile is None else (TILES[tile] if isinstance(tile, str) else int(tile))
+        _check(lib().fp8_mm_with_grid(ctypes.byref(args), t, int(max_workgroups or 0), _stream(stream)))
     return out
 
 

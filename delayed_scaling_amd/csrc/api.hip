@@ -91,10 +91,13 @@ int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* rin
   return launch_quantize(x_bf16, numel, fmt, ring, y_fp8, max_blocks, static_cast<hipStream_t>(stream));
 }
 
-int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_tile(a, -1, stream); }
+int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_grid(a, -1, 0, stream); }
 
-int fp8_mm_with_tile(const fp8_mm_args* a, int tile, void* stream) {
+int fp8_mm_with_tile(const fp8_mm_args* a, int tile, void* stream) { return fp8_mm_with_grid(a, tile, 0, stream); }
+
+int fp8_mm_with_grid(const fp8_mm_args* a, int tile, int max_workgroups, void* stream) {
   if (!a) return set_error(FP8DS_EINVAL, "fp8_mm: args is NULL");
+  if (max_workgroups < 0) return set_error(FP8DS_EINVAL, "fp8_mm: max_workgroups %d < 0", max_workgroups);
   if (!valid_fmt(a->fmt_a) || !valid_fmt(a->fmt_b)) return set_error(FP8DS_EINVAL, "fp8_mm: bad fmt_a/fmt_b");
   if (a->layout < FP8DS_NT || a->layout > FP8DS_TN) return set_error(FP8DS_EINVAL, "fp8_mm: bad layout %d", a->layout);
   if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_F32)
@@ -146,7 +149,7 @@ int fp8_mm_with_tile(const fp8_mm_args* a, int tile, void* stream) {
   p.a_scale_inv = a->a_scale_inv;
   p.b_scale_inv = a->b_scale_inv;
   p.bias = a->bias;
-  return launch_gemm(p, tile, static_cast<hipStream_t>(stream));
+  return launch_gemm(p, tile, max_workgroups, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

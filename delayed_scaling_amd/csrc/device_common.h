@@ -90,18 +90,20 @@ __device__ __forceinline__ v4i rsrc_words(const void* base, uint32_t bytes) {
              (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 
-// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at `voff` in the
-// buffer land at LDS byte lds_base + 16 * lane (lds_base wave-uniform); an
-// offset at or past the buffer size lands as zeros.  Written as inline asm so
-// the compiler does not guard every later LDS read with a wait for all
+// One buffer_load_dwordx4 ... lds: each lane's 16 bytes at byte soff + voff
+// of the buffer land at LDS byte lds_base + 16 * lane (lds_base and soff
+// wave-uniform).  Callers keep soff + voff below 2^32 and the buffer size at
+// least soff + voff for every load meant to read memory; a load whose voff is
+// at or past the buffer size lands as zeros.  Written as inline asm so the
+// compiler does not guard every later LDS read with a wait for all
 // outstanding loads: callers count these loads themselves (vmcnt) and order
 // LDS through barriers.  The instruction writes no VGPR.
-__device__ __forceinline__ void load_lds16(v4i rsrc, uint32_t lds_base, uint32_t voff) {
+__device__ __forceinline__ void load_lds16(v4i rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
                : "memory", "m0");
 #pragma clang diagnostic pop
 }

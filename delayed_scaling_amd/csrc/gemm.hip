@@ -9,24 +9,31 @@
 // tiling (cp.async staging, ldmatrix, PRMT transposes) is prior art only.
 //
 // gfx950 design:
-//  * 4 waves per workgroup in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2)
-//    block of C made of 32 x 32 tiles of v_mfma_f32_32x32x64_f8f6f4.  The
-//    instruction's first source is the B fragment and its second the A
-//    fragment, so each lane ends up holding four consecutive n of one row m:
-//    8-byte bf16 stores and 4-wide bias loads in the epilogue.  The per-operand
-//    format selectors of the instruction take E4M3 x E4M3 and E5M2 x E4M3
-//    (dX, dW) alike.
+//  * Waves in a WGM x WGN grid each own a block of C made of 32 x 32 tiles of
+//    v_mfma_f32_32x32x64_f8f6f4.  The instruction's first source is the B
+//    fragment and its second the A fragment, so each lane ends up holding four
+//    consecutive n of one row m: 8-byte bf16 stores and 4-wide bias loads in
+//    the epilogue.  The per-operand format selectors of the instruction take
+//    E4M3 x E4M3 and E5M2 x E4M3 (dX, dW) alike.
 //  * Operand tiles go global -> LDS with buffer_load ... lds (no VGPR round
-//    trip), 128 K-bytes per stage, two stages.  Loads outside the operand or
-//    past K are given an offset beyond the buffer's size and land as zeros.
-//  * K-contiguous tiles are [rows][128 B] and are read with ds_read_b128;
-//    MN-contiguous (crosswise) tiles are [128 k][BM or BN bytes] and are read
+//    trip), 64 K-bytes per stage, several stages in flight.  Loads outside the
+//    operand or past K get an offset beyond the buffer's size and land as
+//    zeros.
+//  * K-contiguous tiles are [rows][64 B] and are read with ds_read_b128;
+//    MN-contiguous (crosswise) tiles are [64 k][BM or BN bytes] and are read
 //    with ds_read_b64_tr_b8, which transposes 8 x 8-byte blocks across 16
 //    lanes, so crosswise operands need no transpose pass.  16-byte chunks are
 //    XOR-swizzled per row so both read kinds are free of bank conflicts.
-//  * The workgroup -> tile map gives each of the 8 XCDs (workgroups are dealt
-//    to XCDs round-robin) a contiguous run of tiles in grouped order, so the
-//    tiles sharing A rows and B columns meet in one XCD's L2.
+//  * The grid holds as many workgroups as the device runs at once; each runs
+//    every G-th output tile, and its stream of K stages runs on across tile
+//    boundaries, so the loads of the next tile overlap the end of the current
+//    one and its epilogue.
+//  * Tile v runs on XCD v mod 8 (workgroups are dealt to XCDs round-robin);
+//    each XCD gets a contiguous run of tiles in grouped order, so the tiles
+//    sharing A rows and B columns meet in one XCD's L2.
+#include <atomic>
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -70,12 +77,15 @@ __device__ __forceinline__ int swz_mn(int k) {
   else return ((k >> 2) & 1) << 1;
 }
 
-// Workgroup -> (batch, tile row, tile column).
-__device__ __forceinline__ void map_tile(const GemmKArgs& p, int& bt, int& tm, int& tn) {
+// Tile index v -> (batch, tile row, tile column).  Workgroups are dealt to the
+// 8 XCDs round-robin and the grid size is a multiple of 8 whenever a
+// workgroup runs more than one tile, so index v runs on XCD v mod 8: each XCD
+// gets a contiguous run of tiles in grouped order and the tiles sharing A rows
+// and B columns meet in one XCD's L2.
+__device__ __forceinline__ void map_tile(const GemmKArgs& p, int v, int& bt, int& tm, int& tn) {
   const int total = p.tiles_m * p.tiles_n * p.batch;
-  const int w = blockIdx.x;
   const int q = total >> 3, r = total & 7;
-  const int xcd = w & 7, j = w >> 3;
+  const int xcd = v & 7, j = v >> 3;
   const int t = xcd < r ? xcd * (q + 1) + j : r * (q + 1) + (xcd - r) * q + j;
   const int per_batch = p.tiles_m * p.tiles_n;
   bt = t / per_batch;
@@ -84,9 +94,9 @@ __device__ __forceinline__ void map_tile(const GemmKArgs& p, int& bt, int& tm, i
   const int g = u / in_group;
   const int first_m = g * p.group_m;
   const int gsize = min(p.tiles_m - first_m, p.group_m);
-  const int v = u - g * in_group;
-  tm = first_m + v % gsize;
-  tn = v / gsize;
+  const int w = u - g * in_group;
+  tm = first_m + w % gsize;
+  tn = w / gsize;
 }
 
 // 32 rows x 64 k of a K-contiguous tile: lane l gets row base + l%32,
@@ -125,19 +135,28 @@ __device__ __forceinline__ v8i load_frag(const lds_char_t* tile, int base, int l
 }
 
 // Per-lane byte offset of load slot `slot` of an operand tile, for k0 = 0;
-// kOOB for rows / columns outside the operand.  kpos receives the slot's K
-// position inside the stage (checked against K only in the last stage).
+// kOOB for rows / columns outside the operand.
 template <bool KC, int ROWS>
-__device__ __forceinline__ uint32_t slot_offset(int slot, int mn0, int mn_lim, uint32_t ld, int& kpos) {
+__device__ __forceinline__ uint32_t slot_offset(int slot, int mn0, int mn_lim, uint32_t ld) {
   if constexpr (KC) {
     const int row = slot >> 2, pch = slot & 3, lch = pch ^ swz_k(row);
-    kpos = lch << 4;
     return mn0 + row < mn_lim ? (uint32_t)row * ld + (uint32_t)(lch << 4) : kOOB;
   } else {
     constexpr int R = ROWS / 16;
     const int kr = slot / R, pch = slot % R, lch = pch ^ swz_mn<R>(kr);
-    kpos = kr;
     return mn0 + (lch << 4) < mn_lim ? (uint32_t)kr * ld + (uint32_t)(lch << 4) : kOOB;
+  }
+}
+
+// K position, inside its stage, of the bytes load slot `slot` brings in; the
+// slot lies past K in a tail stage when this is >= K mod 64.
+template <bool KC, int ROWS>
+__device__ __forceinline__ int slot_kpos(int slot) {
+  if constexpr (KC) {
+    const int row = slot >> 2, pch = slot & 3;
+    return (pch ^ swz_k(row)) << 4;
+  } else {
+    return slot / (ROWS / 16);
   }
 }
 
@@ -168,199 +187,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int BM, int BN, int WGM, int WGN, int kStages, bool A_KC, bool B_KC, int FA, int FB, int OCC>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
-  constexpr int NW = WGM * WGN, kThreads = 64 * NW;   // waves in a WGM x WGN grid
-  constexpr int WM = BM / WGM, WN = BN / WGN;          // C block of one wave
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK, STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;
-  constexpr int LPS = A_LOADS + B_LOADS;
-  static_assert(TM >= 1 && TN >= 1 && A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * STAGE];
-  lds_char_t* smem = (lds_char_t*)smem_raw;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave % WGM, wn = wave / WGM;
+// Epilogue of one wave for output tile v: y = acc * (sa_inv * sb_inv) +
+// bias[n] with one bf16 rounding.  The wave's C block starts at row r0 and
+// column c0 of the tile; lane l holds rows +l%32 and four consecutive columns
+// per 32 x 32 MFMA tile.
+template <int BM, int BN, int TM, int TN>
+__device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
+                                             int lane) {
   int bt, tmi, tni;
-  map_tile(p, bt, tmi, tni);
-  const int m0 = tmi * BM, n0 = tni * BN;
-
-  const uint32_t a_tile_off = A_KC ? (uint32_t)m0 * p.lda : (uint32_t)m0;
-  const uint32_t b_tile_off = B_KC ? (uint32_t)n0 * p.ldb : (uint32_t)n0;
-  const uint8_t* a_tile = p.a + bt * p.stride_a + a_tile_off;
-  const uint8_t* b_tile = p.b + bt * p.stride_b + b_tile_off;
-  const uint32_t a_rem = p.extent_a - a_tile_off;
-  const uint32_t b_rem = p.extent_b - b_tile_off;
-
-  uint32_t a_voff[A_LOADS], b_voff[B_LOADS];
-  int a_kpos[A_LOADS], b_kpos[B_LOADS];
-#pragma unroll
-  for (int j = 0; j < A_LOADS; ++j)
-    a_voff[j] = slot_offset<A_KC, BM>((j * NW + wave) * 64 + lane, m0, p.m, p.lda, a_kpos[j]);
-#pragma unroll
-  for (int j = 0; j < B_LOADS; ++j)
-    b_voff[j] = slot_offset<B_KC, BN>((j * NW + wave) * 64 + lane, n0, p.n, p.ldb, b_kpos[j]);
-
-  // Global -> LDS loads of K stage kt into LDS buffer kt % kStages: the
-  // scalar part (descriptors, LDS bases) once per stage, then one
-  // buffer_load ... lds per call of issue_one.
-  struct LoadCtx {
-    v4i ra, rb;
-    uint32_t la, lb;
-    int klim;
-    bool tail;
-  };
-  auto load_ctx = [&](int kt, bool tail) __attribute__((always_inline)) {
-    const int k0 = kt * kBK;
-    const uint32_t a_adv = A_KC ? (uint32_t)k0 : (uint32_t)k0 * p.lda;
-    const uint32_t b_adv = B_KC ? (uint32_t)k0 : (uint32_t)k0 * p.ldb;
-    LoadCtx c;
-    c.ra = rsrc_words(a_tile + a_adv, a_rem > a_adv ? a_rem - a_adv : 0u);
-    c.rb = rsrc_words(b_tile + b_adv, b_rem > b_adv ? b_rem - b_adv : 0u);
-    c.la = lds_address(smem + (kt % kStages) * STAGE) + wave * 1024;
-    c.lb = c.la + A_BYTES;
-    c.klim = p.k - k0;
-    c.tail = tail;
-    return c;
-  };
-  auto issue_one = [&](const LoadCtx& c, int j) __attribute__((always_inline)) {
-    if (j < A_LOADS)
-      load_lds16(c.ra, c.la + j * NW * 1024, (c.tail && a_kpos[j] >= c.klim) ? kOOB : a_voff[j]);
-    else
-      load_lds16(c.rb, c.lb + (j - A_LOADS) * NW * 1024,
-                 (c.tail && b_kpos[j - A_LOADS] >= c.klim) ? kOOB : b_voff[j - A_LOADS]);
-  };
-  auto issue = [&](int kt, bool tail) __attribute__((always_inline)) {
-    const LoadCtx c = load_ctx(kt, tail);
-#pragma unroll
-    for (int j = 0; j < LPS; ++j) issue_one(c, j);
-  };
-
-  // The chunk holding K's last bytes also holds the row's padding; zero the
-  // bytes at or past K in the K-contiguous tiles of the last stage (one row
-  // per thread, at most 15 bytes each).
-  auto zero_k_padding = [&](int kt) __attribute__((always_inline)) {
-    const int kin = p.k - kt * kBK;
-    const int c_lo = kin & ~15;
-    lds_char_t* sa = smem + (kt % kStages) * STAGE;
-    constexpr int ROWS = (A_KC ? BM : 0) + (B_KC ? BN : 0);
-    for (int r = threadIdx.x; r < ROWS; r += kThreads) {
-      const bool in_a = A_KC && r < BM;
-      const int row = in_a || !A_KC ? r : r - BM;
-      lds_char_t* rp = sa + (in_a ? 0 : A_BYTES) + row * kBK + (((c_lo >> 4) ^ swz_k(row)) << 4) - c_lo;
-#pragma nounroll
-      for (int b = kin; b < c_lo + 16; ++b) rp[b] = 0;
-    }
-  };
-
-  v16f acc[TN][TM];
-#pragma unroll
-  for (int i = 0; i < TN; ++i)
-#pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
-
-  // Fragments of two consecutive stages live in registers: while the MFMAs
-  // of stage kt run, the LDS reads of stage kt+1 and the global loads of
-  // stage kt+kStages are in flight.
-  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
-  auto read_frags = [&](int kt, v8i (&fa)[TM], v8i (&fb)[TN]) __attribute__((always_inline)) {
-    const lds_char_t* sa = smem + (kt % kStages) * STAGE;
-    const lds_char_t* sb = sa + A_BYTES;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = load_frag<A_KC, BM>(sa, wm * WM + i * 32, lane);
-#pragma unroll
-    for (int i = 0; i < TN; ++i) fb[i] = load_frag<B_KC, BN>(sb, wn * WN + i * 32, lane);
-  };
-  auto mfmas = [&](const v8i (&fa)[TM], const v8i (&fb)[TN]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-      for (int j = 0; j < TM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
-  };
-
-  const int kt_total = (p.k + kBK - 1) / kBK;
-  const int kt_full = p.k / kBK;
-  const bool kfix = (p.k & 15) != 0;
-#pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < kt_total) issue(s, s >= kt_full);
-  if (kt_total > 0) {
-    wait_stages<LPS, kStages>(min(kStages, kt_total) - 1);
-    lds_barrier();
-    if (kfix && kt_full == 0) {
-      zero_k_padding(0);
-      lds_barrier();
-    }
-    read_frags(0, fa0, fb0);
-  }
-
-  // Steady state, two stages per trip with no conditions: make stage kt+1
-  // visible, then issue stage kt's MFMAs one by one, each followed by its
-  // share of the global loads of stage kt+kStages (into the buffer stage kt
-  // freed) and of the LDS reads of stage kt+1's fragments.  Scheduling
-  // barriers keep that interleave: bursts of loads or LDS reads right after
-  // the barrier left the matrix cores idle.  The wave runs at raised priority
-  // while it issues the MFMA stream.
-  constexpr int NM = TM * TN, NF = TM + TN;
-  auto steady = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
-                    __attribute__((always_inline)) {
-    wait_stages<LPS, kStages>(kStages - 2);
-    lds_barrier();
-    const LoadCtx c = load_ctx(kt + kStages, kt + kStages >= kt_full);
-    const lds_char_t* sa = smem + ((kt + 1) % kStages) * STAGE;
-    const lds_char_t* sb = sa + A_BYTES;
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int q = 0; q < NM; ++q) {
-      const int i = q / TM, j = q % TM;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
-#pragma unroll
-      for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) issue_one(c, l);
-#pragma unroll
-      for (int f = q * NF / NM; f < (q + 1) * NF / NM; ++f) {
-        if (f < TM) na[f] = load_frag<A_KC, BM>(sa, wm * WM + f * 32, lane);
-        else nb[f - TM] = load_frag<B_KC, BN>(sb, wn * WN + (f - TM) * 32, lane);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // The last stages: the same with the prefetch and the next reads guarded.
-  auto drain = [&](int kt, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM], v8i (&nb)[TN])
-                   __attribute__((always_inline)) {
-    if (kt + 1 < kt_total) {
-      wait_stages<LPS, kStages>(min(kt + kStages - 1, kt_total - 1) - (kt + 1));
-      lds_barrier();
-      if (kfix && kt + 1 == kt_full) {
-        zero_k_padding(kt + 1);
-        lds_barrier();
-      }
-      if (kt + kStages < kt_total) issue(kt + kStages, kt + kStages >= kt_full);
-      read_frags(kt + 1, na, nb);
-    }
-    mfmas(fa, fb);
-  };
-  int kt = 0;
-  for (; kt + kStages + 1 < kt_total; kt += 2) {
-    steady(kt, fa0, fb0, fa1, fb1);
-    steady(kt + 1, fa1, fb1, fa0, fb0);
-  }
-  for (; kt < kt_total; kt += 2) {
-    drain(kt, fa0, fb0, fa1, fb1);
-    if (kt + 1 < kt_total) drain(kt + 1, fa1, fb1, fa0, fb0);
-  }
-
-  // Epilogue: y = acc * (sa_inv * sb_inv) + bias[n], one bf16 rounding.
+  map_tile(p, v, bt, tmi, tni);
+  const int m0 = tmi * BM + r0, n0 = tni * BN + c0;
   const float alpha = p.a_scale_inv[0] * p.b_scale_inv[0];
   uint16_t* cb = p.c + bt * p.stride_c;
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const int n = n0 + wn * WN + i * 32 + 8 * rq + 4 * (lane >> 5);
+      const int n = n0 + i * 32 + 8 * rq + 4 * (lane >> 5);
       if (n >= p.n) continue;
       float bias4[4] = {0.f, 0.f, 0.f, 0.f};
       const bool full4 = n + 3 < p.n;
@@ -388,7 +231,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
       }
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const int m = m0 + wm * WM + j * 32 + (lane & 31);
+        const int m = m0 + j * 32 + (lane & 31);
         if (m >= p.m) continue;
         const float y0 = __builtin_fmaf(acc[i][j][4 * rq + 0], alpha, bias4[0]);
         const float y1 = __builtin_fmaf(acc[i][j][4 * rq + 1], alpha, bias4[1]);
@@ -399,13 +242,293 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
           *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
         } else {
           const uint32_t lo = pack_bf16x2(y0, y1), hi = pack_bf16x2(y2, y3);
-          const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+          const uint16_t v4[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
           for (int e = 0; e < 4; ++e)
-            if (n + e < p.n) dst[e] = v[e];
+            if (n + e < p.n) dst[e] = v4[e];
         }
       }
     }
   }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero_acc(v16f (&acc)[TN][TM]) {
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
+}
+
+// Global -> LDS side of a workgroup that runs the output tiles blockIdx.x,
+// blockIdx.x + G, ... (G = grid size) as one stream of K stages of kBK bytes.
+// Stage s lands in LDS buffer s % kStages as [A tile | B tile]; each of the
+// NW waves brings 1 KiB per buffer_load ... lds.  The next stage to issue is
+// stage k of the workgroup's tile number it.  Each tile's operand strips get
+// one buffer descriptor spanning the rest of the operand from the strip's
+// start; a stage adds its K offset as the loads' scalar offset.  Past the
+// workgroup's last tile the descriptors are empty: those loads fetch nothing
+// and land zeros, so every stage issues the same number of loads and vmcnt
+// counts stay fixed.
+template <int BM, int BN, int NW, int kStages, bool A_KC, bool B_KC>
+struct TileLoader {
+  static constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK, STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;
+  static constexpr int LPS = A_LOADS + B_LOADS;   // loads per wave and stage
+  static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
+
+  int it = 0, k = 0;
+  uint32_t s = 0;
+  v4i ra, rb;
+  uint32_t a_voff[A_LOADS], b_voff[B_LOADS];
+  uint32_t tail_oob = 0;   // bit j: this lane's load j lies past K in a tail stage
+
+  struct Ctx {
+    uint32_t sa, sb, la, lb;
+    bool tail;
+  };
+
+  __device__ __forceinline__ void set_tile(const GemmKArgs& p, int v, int wave, int lane) {
+    int bt, tmi, tni;
+    map_tile(p, v, bt, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const uint32_t a_tile_off = A_KC ? (uint32_t)m0 * p.lda : (uint32_t)m0;
+    const uint32_t b_tile_off = B_KC ? (uint32_t)n0 * p.ldb : (uint32_t)n0;
+    ra = rsrc_words(p.a + bt * p.stride_a + a_tile_off, p.extent_a - a_tile_off);
+    rb = rsrc_words(p.b + bt * p.stride_b + b_tile_off, p.extent_b - b_tile_off);
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      a_voff[j] = slot_offset<A_KC, BM>((j * NW + wave) * 64 + lane, m0, p.m, p.lda);
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      b_voff[j] = slot_offset<B_KC, BN>((j * NW + wave) * 64 + lane, n0, p.n, p.ldb);
+  }
+
+  __device__ __forceinline__ void init(const GemmKArgs& p, int wave, int lane, int kt_full) {
+    // The same for every tile, as all tiles share K.
+#pragma unroll
+    for (int j = 0; j < A_LOADS; ++j)
+      tail_oob |= (uint32_t)(slot_kpos<A_KC, BM>((j * NW + wave) * 64 + lane) >= p.k - kt_full * kBK) << j;
+#pragma unroll
+    for (int j = 0; j < B_LOADS; ++j)
+      tail_oob |= (uint32_t)(slot_kpos<B_KC, BN>((j * NW + wave) * 64 + lane) >= p.k - kt_full * kBK)
+                  << (A_LOADS + j);
+    set_tile(p, blockIdx.x, wave, lane);
+  }
+
+  // Scalar part of the next stage's loads: K offsets and LDS bases.
+  __device__ __forceinline__ Ctx ctx(const GemmKArgs& p, const lds_char_t* smem, int wave, int kt_full) const {
+    const uint32_t k0 = (uint32_t)k * kBK;
+    Ctx c;
+    c.sa = A_KC ? k0 : k0 * p.lda;
+    c.sb = B_KC ? k0 : k0 * p.ldb;
+    c.la = lds_address(smem + (s % kStages) * STAGE) + wave * 1024;
+    c.lb = c.la + A_BYTES;
+    c.tail = k >= kt_full;
+    return c;
+  }
+
+  __device__ __forceinline__ void issue_one(const Ctx& c, int j) const {
+    const bool oob = c.tail && ((tail_oob >> j) & 1u);
+    if (j < A_LOADS)
+      load_lds16(ra, c.la + j * NW * 1024, oob ? kOOB : a_voff[j], c.sa);
+    else
+      load_lds16(rb, c.lb + (j - A_LOADS) * NW * 1024, oob ? kOOB : b_voff[j - A_LOADS], c.sb);
+  }
+
+  __device__ __forceinline__ void advance(const GemmKArgs& p, int my_tiles, int kt_total, int wave, int lane) {
+    ++s;
+    if (++k == kt_total) {
+      k = 0;
+      if (++it < my_tiles) {
+        set_tile(p, blockIdx.x + it * gridDim.x, wave, lane);
+      } else {
+        ra[2] = 0;
+        rb[2] = 0;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void issue_next(const GemmKArgs& p, const lds_char_t* smem, int my_tiles, int kt_total,
+                                             int kt_full, int wave, int lane) {
+    const Ctx c = ctx(p, smem, wave, kt_full);
+#pragma unroll
+    for (int j = 0; j < LPS; ++j) issue_one(c, j);
+    advance(p, my_tiles, kt_total, wave, lane);
+  }
+};
+
+// The chunk holding K's last bytes also holds the row's padding; zero the
+// bytes at or past K in the K-contiguous tiles of a tail stage's LDS buffer
+// (one row per thread, at most 15 bytes each).
+template <int BM, int BN, bool A_KC, bool B_KC, int kThreads>
+__device__ __forceinline__ void zero_k_padding(lds_char_t* stage_buf, int k, int kt_full) {
+  constexpr int A_BYTES = BM * kBK;
+  const int kin = k - kt_full * kBK;
+  const int c_lo = kin & ~15;
+  constexpr int ROWS = (A_KC ? BM : 0) + (B_KC ? BN : 0);
+  for (int r = threadIdx.x; r < ROWS; r += kThreads) {
+    const bool in_a = A_KC && r < BM;
+    const int row = in_a || !A_KC ? r : r - BM;
+    lds_char_t* rp = stage_buf + (in_a ? 0 : A_BYTES) + row * kBK + (((c_lo >> 4) ^ swz_k(row)) << 4) - c_lo;
+#pragma nounroll
+    for (int b = kin; b < c_lo + 16; ++b) rp[b] = 0;
+  }
+}
+
+// One wave's fragments of a stage: TM 32-row A fragments from row r0 and TN
+// 32-column B fragments from column c0 of the tile.
+template <int BM, int BN, int TM, int TN, bool A_KC, bool B_KC>
+__device__ __forceinline__ void read_frags(const lds_char_t* stage_buf, int r0, int c0, int lane, v8i (&fa)[TM],
+                                           v8i (&fb)[TN]) {
+  const lds_char_t* sb = stage_buf + BM * kBK;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) fa[i] = load_frag<A_KC, BM>(stage_buf, r0 + i * 32, lane);
+#pragma unroll
+  for (int i = 0; i < TN; ++i) fb[i] = load_frag<B_KC, BN>(sb, c0 + i * 32, lane);
+}
+
+template <int TM, int TN, int FA, int FB>
+__device__ __forceinline__ void mfmas(v16f (&acc)[TN][TM], const v8i (&fa)[TM], const v8i (&fb)[TN]) {
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+}
+
+// General kernel: any tile of the family, any K.  Waves in a WGM x WGN grid
+// each own a (BM/WGM) x (BN/WGN) block of the tile.  Every wave runs all
+// stages: wait for stage s+1, barrier, then stage s's MFMAs interleaved with
+// the loads of stage s+kStages and the LDS reads of stage s+1's fragments.
+template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC, bool B_KC, int FA, int FB>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
+  constexpr int NW = WGM * WGN, kThreads = 64 * NW;   // waves in a WGM x WGN grid
+  constexpr int WM = BM / WGM, WN = BN / WGN;          // C block of one wave
+  constexpr int TM = WM / 32, TN = WN / 32;
+  using Loader = TileLoader<BM, BN, NW, kStages, A_KC, B_KC>;
+  constexpr int STAGE = Loader::STAGE, LPS = Loader::LPS;
+  static_assert(TM >= 1 && TN >= 1, "tile too small");
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * STAGE];
+  lds_char_t* smem = (lds_char_t*)smem_raw;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = (wave % WGM) * WM, c0 = (wave / WGM) * WN;
+
+  // The loads of a tile's first stages go out while the previous tile's last
+  // stages compute, so the operand pipeline never drains between tiles and
+  // the epilogue's stores overlap the loads.
+  const int G = gridDim.x;
+  const int total = p.tiles_m * p.tiles_n * p.batch;
+  const int my_tiles = (total - 1 - (int)blockIdx.x) / G + 1;
+  const int kt_total = (p.k + kBK - 1) / kBK;
+  const int kt_full = p.k / kBK;
+  const bool kfix = (p.k & 15) != 0;
+
+  v16f acc[TN][TM];
+  zero_acc(acc);
+  if (kt_total == 0) {          // K = 0: every output is bf16(bias) or zero
+    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane);
+    return;
+  }
+
+  Loader ld;
+  ld.init(p, wave, lane, kt_full);
+  auto buf = [&](uint32_t st) __attribute__((always_inline)) { return smem + (st % kStages) * STAGE; };
+
+  // Stage s+1 is visible to the whole workgroup: zero its K padding first if
+  // it is a tail stage (K position next_k) of a K that is not a multiple of 16.
+  auto fix_tail = [&](int s, int next_k) __attribute__((always_inline)) {
+    if (kfix && next_k == kt_full) {
+      zero_k_padding<BM, BN, A_KC, B_KC, kThreads>(buf(s + 1), p.k, kt_full);
+      lds_barrier();
+    }
+  };
+
+  // Fragments of two consecutive stages live in registers: while the MFMAs
+  // of stage s run, the LDS reads of stage s+1 and the global loads of stage
+  // s+kStages are in flight.
+  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+
+  // One stage s: make stage s+1 visible, then issue stage s's MFMAs one by
+  // one, each followed by its share of the global loads of stage s+kStages
+  // (into the buffer stage s freed) and, when READ, of the LDS reads of stage
+  // s+1's fragments into na / nb.  Scheduling barriers keep that interleave:
+  // bursts of loads or LDS reads right after the barrier left the matrix cores
+  // idle.  The wave runs at raised priority while it issues the MFMA stream.
+  constexpr int NM = TM * TN, NF = TM + TN;
+  auto stage = [&](auto read, int s, int next_k, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM],
+                   v8i (&nb)[TN]) __attribute__((always_inline)) {
+    constexpr bool READ = decltype(read)::value;
+    wait_stages<LPS, kStages>(kStages - 2);
+    lds_barrier();
+    fix_tail(s, next_k);
+    const typename Loader::Ctx c = ld.ctx(p, smem, wave, kt_full);
+    const lds_char_t* sa = buf(s + 1);
+    const lds_char_t* sb = sa + Loader::A_BYTES;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int i = q / TM, j = q % TM;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+#pragma unroll
+      for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) ld.issue_one(c, l);
+      if constexpr (READ) {
+#pragma unroll
+        for (int f = q * NF / NM; f < (q + 1) * NF / NM; ++f) {
+          if (f < TM) na[f] = load_frag<A_KC, BM>(sa, r0 + f * 32, lane);
+          else nb[f - TM] = load_frag<B_KC, BN>(sb, c0 + (f - TM) * 32, lane);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    ld.advance(p, my_tiles, kt_total, wave, lane);
+  };
+  using Read = std::true_type;
+  using NoRead = std::false_type;
+
+  // Prologue: stages 0 .. kStages-1 in flight, stage 0's fragments in set 0.
+#pragma unroll
+  for (int st = 0; st < kStages; ++st) ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
+  wait_stages<LPS, kStages>(kStages - 1);
+  lds_barrier();
+  if (kfix && kt_full == 0) {
+    zero_k_padding<BM, BN, A_KC, B_KC, kThreads>(buf(0), p.k, kt_full);
+    lds_barrier();
+  }
+  read_frags<BM, BN, TM, TN, A_KC, B_KC>(buf(0), r0, c0, lane, fa0, fb0);
+
+  // Each tile starts with its first stage's fragments in set 0 and runs its
+  // kt_total - 1 leading stages in pairs that alternate the two fragment
+  // sets (one single stage first when their count is odd, its fragments
+  // moved back to set 0).  Its last stage runs the MFMAs and the loads only;
+  // then the tile is stored, the accumulators cleared, and the next stage's
+  // fragments read into set 0, so the epilogue has the registers of both
+  // fragment sets to itself.
+  for (int it = 0; it < my_tiles; ++it) {
+    const int s0 = it * kt_total;
+    int kt = 0;
+    if ((kt_total - 1) & 1) {
+      stage(Read{}, s0, 1, fa0, fb0, fa1, fb1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa0[i] = fa1[i];
+#pragma unroll
+      for (int i = 0; i < TN; ++i) fb0[i] = fb1[i];
+      kt = 1;
+    }
+    for (; kt < kt_total - 1; kt += 2) {
+      stage(Read{}, s0 + kt, kt + 1, fa0, fb0, fa1, fb1);
+      stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
+    }
+    stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
+    store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane);
+    zero_acc(acc);
+    read_frags<BM, BN, TM, TN, A_KC, B_KC>(buf(s0 + kt_total), r0, c0, lane, fa0, fb0);
+  }
+  // The loads of the stages past the last tile write this workgroup's LDS:
+  // let them land before the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ---------------------------------------------------------------------------
@@ -417,27 +540,29 @@ struct TileCfg {
 // Tile family (index = the tile argument of fp8_mm_with_tile).  256x256 with
 // four waves runs one workgroup per CU (4 LDS stages, 128 KiB), each wave a
 // 128x128 block; the eight-wave 256x256 tiles give every SIMD two waves of a
-// 128x64 / 64x128 block so one wave's memory stalls hide behind the other's
-// MFMAs; 256x128 / 128x256 run two workgroups per CU (3 stages, 72 KiB
-// each); 128x128 and 64x64 serve problems too small to fill the chip.
+// 128x64 / 64x128 block; 256x128 / 128x256 run two workgroups per CU (3
+// stages, 72 KiB each); 128x128 and 64x64 serve problems too small to fill
+// the chip.
 constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
                               {128, 256, 4}, {256, 256, 8}, {256, 256, 8}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 typedef void (*GemmFn)(GemmKArgs);
 
+#define FP8DS_FMT_CASES(KERNEL, AKC, BKC, ...)                     \
+  if (fa == 0 && fb == 0) return KERNEL<__VA_ARGS__ AKC, BKC, 0, 0>; \
+  if (fa == 1 && fb == 0) return KERNEL<__VA_ARGS__ AKC, BKC, 1, 0>; \
+  if (fa == 0 && fb == 1) return KERNEL<__VA_ARGS__ AKC, BKC, 0, 1>; \
+  return KERNEL<__VA_ARGS__ AKC, BKC, 1, 1>;
+
 template <int BM, int BN, int WGM, int WGN, int ST, int OCC>
 GemmFn pick_kernel(int layout, int fa, int fb) {
-#define FP8DS_FMT_CASES(AKC, BKC)                                                              \
-  if (fa == 0 && fb == 0) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 0, 0, OCC>;       \
-  if (fa == 1 && fb == 0) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 1, 0, OCC>;       \
-  if (fa == 0 && fb == 1) return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 0, 1, OCC>;       \
-  return gemm_kernel<BM, BN, WGM, WGN, ST, AKC, BKC, 1, 1, OCC>;
-  if (layout == 0) { FP8DS_FMT_CASES(true, true) }
-  if (layout == 1) { FP8DS_FMT_CASES(true, false) }
-  FP8DS_FMT_CASES(false, false)
-#undef FP8DS_FMT_CASES
+  if (layout == 0) { FP8DS_FMT_CASES(gemm_kernel, true, true, BM, BN, WGM, WGN, ST, OCC,) }
+  if (layout == 1) { FP8DS_FMT_CASES(gemm_kernel, true, false, BM, BN, WGM, WGN, ST, OCC,) }
+  FP8DS_FMT_CASES(gemm_kernel, false, false, BM, BN, WGM, WGN, ST, OCC,)
 }
+
+#undef FP8DS_FMT_CASES
 
 GemmFn kernel_for(int tile, int layout, int fa, int fb) {
   switch (tile) {
@@ -453,10 +578,9 @@ GemmFn kernel_for(int tile, int layout, int fa, int fb) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Largest tile whose grid still fills the 256 CUs; else the one with most tiles.
+// Largest tile whose grid still fills the 256 CUs, else the one with most
+// tiles.  For the 256x256 size the eight-wave variant measured faster.
 int choose_tile(const GemmProblem& p) {
-  // Largest tile whose grid still fills the 256 CUs, else the one with most
-  // tiles.  For the 256x256 size the eight-wave variant measured faster.
   constexpr int64_t kCUs = 256;
   constexpr int order[] = {6, 1, 2};
   for (int t : order) {
@@ -466,9 +590,28 @@ int choose_tile(const GemmProblem& p) {
   return 2;
 }
 
+// Workgroups of one kernel that fit on the device at once (CUs x occupancy),
+// cached per device and kernel.
+int resident_workgroups(GemmFn fn, int slot, int threads) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][kNumTiles * 12];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  const int hit = cache[dev][slot].load(std::memory_order_relaxed);
+  if (hit > 0) return hit;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
+          hipSuccess)
+    return 0;
+  const int r = cus * per_cu;
+  if (r > 0) cache[dev][slot].store(r, std::memory_order_relaxed);
+  return r;
+}
+
 }  // namespace
 
-int launch_gemm(const GemmProblem& p, int tile_override, hipStream_t stream) {
+int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hipStream_t stream) {
   const int t = (tile_override >= 0 && tile_override < kNumTiles) ? tile_override : choose_tile(p);
   GemmKArgs k{};
   k.a = p.a;
@@ -496,7 +639,16 @@ int launch_gemm(const GemmProblem& p, int tile_override, hipStream_t stream) {
   const int64_t total = (int64_t)k.tiles_m * k.tiles_n * k.batch;
   if (total > 0x7FFFFFFF) return set_error(-3, "fp8_mm: %lld tiles exceed the grid limit", (long long)total);
   GemmFn fn = kernel_for(t, p.layout, p.fmt_a, p.fmt_b);
-  hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(64 * kTiles[t].waves), 0, stream, k);
+  const int threads = 64 * kTiles[t].waves;
+  // One workgroup per resident slot, each running every G-th tile; G a
+  // multiple of 8 keeps tile v on XCD v mod 8.
+  int64_t g = max_workgroups > 0 ? max_workgroups : resident_workgroups(fn, t * 12 + p.layout * 4 + p.fmt_a * 2 + p.fmt_b, threads);
+  if (g <= 0) g = total;
+  if (g < total && g >= 8) g &= ~int64_t(7);
+  if (g > total) g = total;
+  if (cdiv(total, g) * cdiv(p.k, 64) > 0x7FFFFFFF)
+    return set_error(-3, "fp8_mm: %lld K stages per workgroup exceed the kernel's counter", (long long)(cdiv(total, g) * cdiv(p.k, 64)));
+  hipLaunchKernelGGL(fn, dim3((unsigned)g), dim3(threads), 0, stream, k);
   return check_launch("gemm_kernel");
 }
 

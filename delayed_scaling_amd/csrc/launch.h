@@ -29,6 +29,8 @@ struct GemmProblem {
   const void* bias;
 };
 
-int launch_gemm(const GemmProblem& p, int tile_override, hipStream_t stream);
+// tile_override < 0 picks the tile; max_workgroups <= 0 sizes the grid to the
+// workgroups the device holds at once.
+int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hipStream_t stream);
 
 }  // namespace fp8ds

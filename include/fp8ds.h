@@ -150,9 +150,18 @@ int fp8_mm(const fp8_mm_args* args, void* stream);
 
 /* fp8_mm with the workgroup tile forced: tile = index into the tile family
  * (M x N: 0: 256x256, 1: 128x128, 2: 64x64, 3: 256x128, 4: 128x256, 5 and 6:
- * 256x256 with eight waves), -1 = the automatic choice.  Same
- * results within the tolerance of fp8_mm; for tests and tuning sweeps. */
+ * 256x256 with eight waves), -1 or any index outside 0..6 = the automatic
+ * choice.  Every tile accumulates each output over K in the same order, so
+ * all tiles give the same bits; for tests and tuning sweeps. */
 int fp8_mm_with_tile(const fp8_mm_args* args, int tile, void* stream);
+
+/* fp8_mm_with_tile with the grid bounded: at most max_workgroups workgroups,
+ * each running every G-th output tile in turn (G = the grid size); 0 = as
+ * many as the device holds at once (what fp8_mm uses).  Results are the
+ * same bits as fp8_mm_with_tile with the same tile; for tests that need one
+ * workgroup to run several tiles on small problems, and for tuning.
+ * max_workgroups < 0 or > 2^31-1 is FP8DS_EINVAL. */
+int fp8_mm_with_grid(const fp8_mm_args* args, int tile, int max_workgroups, void* stream);
 
 /* Message of the last non-zero status returned on the calling thread. */
 const char* fp8_last_error(void);

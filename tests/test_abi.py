@@ -85,6 +85,8 @@ def test_validation_errors_launch_nothing(L):
     args.bias_kind = 1                                                            # bias kind without pointer
     assert L.fp8_mm(ctypes.byref(args), None) == -1
     args.bias_kind = 0
+    assert L.fp8_mm_with_grid(ctypes.byref(args), -1, -1, None) == -1             # negative grid bound
+    assert b"max_workgroups" in L.fp8_last_error()
     args.m = 1 << 31
     assert L.fp8_mm(ctypes.byref(args), None) == -1
     args.m, args.k, args.lda, args.ldb = 1 << 20, 1 << 12, 1 << 12, 1 << 12       # 4 GiB operand

@@ -40,7 +40,7 @@ def scale_tensor(v):
 
 
 def run_case(ds, layout, fa, fb, m, n, k, batch=1, bcast_b=False, bias_kind=None, tile=None,
-             pad_ld=0, seed=0, codes=None, sa=0.013, sb=0.021):
+             pad_ld=0, seed=0, codes=None, sa=0.013, sb=0.021, grid=None):
     (ar, ac), (br, bc) = stored_shapes(layout, m, n, k)
     up = lambda v, q: (v + q - 1) // q * q
     lda, ldb, ldc = up(ac, 16) + pad_ld, up(bc, 16) + pad_ld, up(n, 8) + (8 if pad_ld else 0)
@@ -61,7 +61,7 @@ def run_case(ds, layout, fa, fb, m, n, k, batch=1, bcast_b=False, bias_kind=None
     out = out.view(torch.bfloat16)
     ds.fp8_mm(to_dev_u8(a), to_dev_u8(b), fa, fb, layout, m, n, k, scale_tensor(sa), scale_tensor(sb),
               bias=bias, out=out, batch=batch, lda=lda, ldb=ldb, ldc=ldc, stride_a=stride_a,
-              stride_b=stride_b, stride_c=stride_c, tile=tile)
+              stride_b=stride_b, stride_c=stride_c, tile=tile, max_workgroups=grid)
     torch.cuda.synchronize()
     raw = bf16_bits(out)
     y, ref = oracle.mm(a, b, fa, fb, layout, m, n, k, lda, ldb, sa, sb, bias_np, batch, stride_a, stride_b)
@@ -71,7 +71,7 @@ def run_case(ds, layout, fa, fb, m, n, k, batch=1, bcast_b=False, bias_kind=None
     assert np.all(full[:, :, n:] == canary) and np.all(raw[batch * stride_c:] == canary)
     amax_a = oracle.max_abs_dequant(a, fa, sa)
     amax_b = oracle.max_abs_dequant(b, fb, sb)
-    check_close(got, ref, k, amax_a, amax_b, (layout, fa, fb, m, n, k, batch, tile))
+    check_close(got, ref, k, amax_a, amax_b, (layout, fa, fb, m, n, k, batch, tile, grid))
     return got, ref
 
 
@@ -85,6 +85,23 @@ def test_layouts_formats_tiles_ragged(tile, layout, fa, fb):
     run_case(ds, LAYOUTS[layout], fa, fb, 300, 520, 320, tile=tile, bias_kind="bf16", seed=7)
     # K not a multiple of 16 (zero-fixed padding), padded leading dimensions
     run_case(ds, LAYOUTS[layout], fa, fb, 130, 90, 200, tile=tile, pad_ld=16, seed=8)
+
+
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_workgroups_running_several_tiles(tile, layout):
+    """Grids of 1, 3 and 8 workgroups: each workgroup runs many output tiles
+    back to back, its loads running ahead into its next tile while the
+    current one computes and stores."""
+    ds = require_gpu()
+    say(f"gemm {layout} tile={tile} bounded grids")
+    lay = LAYOUTS[layout]
+    run_case(ds, lay, 1, 0, 300, 520, 320, tile=tile, bias_kind="f32", seed=30, grid=8)     # 5 stages per tile
+    run_case(ds, lay, 0, 0, 130, 90, 200, tile=tile, pad_ld=16, seed=31, grid=3)           # K % 16 != 0, 4 stages
+    run_case(ds, lay, 0, 1, 200, 136, 64, tile=tile, seed=32, grid=1)                      # one stage per tile
+    run_case(ds, lay, 1, 1, 270, 300, 336, tile=tile, seed=34, grid=8)                     # last stage 16 of 64
+    run_case(ds, lay, 0, 0, 96, 200, 128, batch=5, bcast_b=True, bias_kind="bf16", tile=tile, seed=33,
+             grid=8)                                                                        # 2 stages, batches
 
 
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
@@ -120,5 +137,8 @@ def test_deterministic_per_tile():
     for tile in ["256x256", "128x128", "64x64", "256x256w8"]:
         o1 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile)
         o2 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile)
+        o3 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile,
+                       max_workgroups=3)
         torch.cuda.synchronize()
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+        assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))   # grid size never changes the bits
