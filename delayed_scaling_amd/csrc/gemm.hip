@@ -42,6 +42,7 @@ namespace fp8ds {
 namespace {
 
 constexpr int kBK = 64;           // K bytes (= elements) per pipeline stage
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every buffer: loads give zero
 
 struct GemmKArgs {
@@ -58,6 +59,7 @@ struct GemmKArgs {
   const float* b_scale_inv;
   const void* bias;
   int bias_kind;
+  int ldc_small;   // 256 * ldc < 2^31: offsets inside a tile fit 32 bits
 };
 
 // K-contiguous tile [rows][64 B]: 16-byte chunk c of row r sits at chunk
@@ -187,18 +189,64 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Epilogue of one wave for output tile v: y = acc * (sa_inv * sb_inv) +
-// bias[n] with one bf16 rounding.  The wave's C block starts at row r0 and
-// column c0 of the tile; lane l holds rows +l%32 and four consecutive columns
-// per 32 x 32 MFMA tile.
+// Lanes l and l+32 hold the same row; lane l+32 holds the four columns after
+// lane l's in each 8-column group.  This swaps a value between the two lane
+// halves (v_permlane32_swap): lane l receives lane l+32's value and the
+// other way round.
+__device__ __forceinline__ uint32_t swap_lane_halves(uint32_t x, bool hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return hi ? r[0] : r[1];
+}
+
+// Epilogue of one wave for output tile v: y = acc * alpha + bias[n] with one
+// bf16 rounding, alpha = sa_inv * sb_inv.  The wave's C block starts at row
+// r0 and column c0 of the tile; lane l holds rows +l%32 and four consecutive
+// columns per 8-column group of each 32 x 32 MFMA tile.
+//
+// A block inside C with no bias takes the fast path: two column groups are
+// combined by swapping half of them between the lane halves, so every lane
+// stores 8 consecutive columns (16 bytes) and each store instruction writes
+// 32 rows x 32 contiguous bytes, with offsets relative to the block's scalar
+// base.  It issues no loads, so nothing waits on the loads of the next tile
+// that are already in flight.  Edge blocks and bias go through the guarded
+// path, whose bias loads make the wave wait for those loads.
 template <int BM, int BN, int TM, int TN>
 __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
-                                             int lane) {
+                                             int lane, float alpha) {
   int bt, tmi, tni;
   map_tile(p, v, bt, tmi, tni);
   const int m0 = tmi * BM + r0, n0 = tni * BN + c0;
-  const float alpha = p.a_scale_inv[0] * p.b_scale_inv[0];
   uint16_t* cb = p.c + bt * p.stride_c;
+  // (Blocks of more than 8 MFMA tiles keep their accumulators in AGPRs; for
+  // them the fast path's extra registers cost more than it saves.)
+  if (TM * TN <= 8 && p.bias_kind == 0 && p.ldc_small && m0 + TM * 32 <= p.m && n0 + TN * 32 <= p.n) {
+    uint8_t* base = reinterpret_cast<uint8_t*>(cb + (int64_t)m0 * p.ldc + n0);
+    const bool hi = lane >= 32;
+    const uint32_t ldc = (uint32_t)p.ldc;
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+#pragma unroll
+      for (int rq = 0; rq < 4; rq += 2) {
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          const v16f& a = acc[i][j];
+          const uint32_t g0a = pack_bf16x2(__builtin_fmaf(a[4 * rq + 0], alpha, 0.f), __builtin_fmaf(a[4 * rq + 1], alpha, 0.f));
+          const uint32_t g0b = pack_bf16x2(__builtin_fmaf(a[4 * rq + 2], alpha, 0.f), __builtin_fmaf(a[4 * rq + 3], alpha, 0.f));
+          const uint32_t g1a = pack_bf16x2(__builtin_fmaf(a[4 * rq + 4], alpha, 0.f), __builtin_fmaf(a[4 * rq + 5], alpha, 0.f));
+          const uint32_t g1b = pack_bf16x2(__builtin_fmaf(a[4 * rq + 6], alpha, 0.f), __builtin_fmaf(a[4 * rq + 7], alpha, 0.f));
+          // lane l keeps group rq and gets lane l+32's half of it; lane l+32
+          // keeps group rq+1 and gets lane l's half of that one.
+          const uint32_t ra = swap_lane_halves(hi ? g0a : g1a, hi);
+          const uint32_t rb = swap_lane_halves(hi ? g0b : g1b, hi);
+          const u32x4 out = hi ? u32x4{ra, rb, g1a, g1b} : u32x4{g0a, g0b, ra, rb};
+          const uint32_t col = (uint32_t)(i * 32 + 8 * (rq + (hi ? 1 : 0)));
+          const uint32_t off = ((uint32_t)(j * 32 + (lane & 31)) * ldc + col) * 2u;
+          *reinterpret_cast<u32x4*>(base + off) = out;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
 #pragma unroll
@@ -425,10 +473,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
   const int kt_full = p.k / kBK;
   const bool kfix = (p.k & 15) != 0;
 
+  // The dequantization factor, read before any operand load is in flight.
+  const float alpha = __builtin_bit_cast(
+      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, p.a_scale_inv[0] * p.b_scale_inv[0])));
+
   v16f acc[TN][TM];
   zero_acc(acc);
   if (kt_total == 0) {          // K = 0: every output is bf16(bias) or zero
-    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane);
+    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane, alpha);
     return;
   }
 
@@ -522,7 +574,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
       stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
     }
     stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
-    store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane);
+    store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane, alpha);
     zero_acc(acc);
     read_frags<BM, BN, TM, TN, A_KC, B_KC>(buf(s0 + kt_total), r0, c0, lane, fa0, fb0);
   }
@@ -636,6 +688,7 @@ int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hip
   k.b_scale_inv = p.b_scale_inv;
   k.bias = p.bias;
   k.bias_kind = p.bias_kind;
+  k.ldc_small = p.ldc * 256 < 0x80000000LL;
   const int64_t total = (int64_t)k.tiles_m * k.tiles_n * k.batch;
   if (total > 0x7FFFFFFF) return set_error(-3, "fp8_mm: %lld tiles exceed the grid limit", (long long)total);
   GemmFn fn = kernel_for(t, p.layout, p.fmt_a, p.fmt_b);
