@@ -23,6 +23,12 @@ import numpy as np
 E4M3 = 0
 E5M2 = 1
 
+# Element types a quantize may read (fp8.py history @f4c44ebf, entry that
+# templates the quantize on its input type: bf16, fp16 or fp32).
+IN_BF16 = 0
+IN_F16 = 1
+IN_F32 = 2
+
 # Largest finite magnitude: E4M3 (1 + 6/8) * 2^8 = 448, E5M2 (1 + 3/4) * 2^15.
 FMAX = {E4M3: 448.0, E5M2: 57344.0}
 
@@ -138,6 +144,18 @@ def f64_to_bf16(y):
     bits = np.where(nan, np.uint16(0x7FC0), bits)
     bits = bits | (sign.astype(np.uint16) << np.uint16(15))
     return bits.astype(np.uint16).reshape(y.shape)
+
+
+def input_to_f32(bits, kind):
+    """float32 values of input elements given as raw bits: bf16 and fp16
+    (uint16 patterns) widen exactly, fp32 (uint32 patterns) is reinterpreted."""
+    if kind == IN_BF16:
+        return bf16_to_f32(bits)
+    if kind == IN_F16:
+        return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+    if kind == IN_F32:
+        return np.asarray(bits, dtype=np.uint32).view(np.float32)
+    raise ValueError("kind must be IN_BF16, IN_F16 or IN_F32")
 
 
 def bf16_ulp(bits):

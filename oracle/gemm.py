@@ -16,11 +16,16 @@ astrai/extension/fp8.py):
   * the linear layer runs its forward on the congruous layout and dX / dW on
     crosswise operands (crosswise-B / crosswise-A entries).
 
+  * the bias may be stored as 8-bit codes with a scale of its own, dequantized
+    in the epilogue after the operand scaling (history of test_fp8_mma.py,
+    bias_scale entry).
+
 Definition used here (the reading of "fp32 accumulate" as an approximation of
 the exact sum): for every batch b, row m, column n
     acc = sum_k dec(A)[m,k] * dec(B)[k,n]                (float64)
     y   = acc * sa_inv * sb_inv + fl32(bias[n])         (float64)
     out = bf16_round_nearest_even(y)                    (straight from float64)
+where an 8-bit bias contributes the float32 product fl32(dec(code) * bias_scale_inv).
 Layouts (row-major storage, leading dimensions in elements, batch strides in
 elements):
     NT: A stored [M, K] (A[m,k] = a[m*lda + k]),  B stored [N, K] (b[n*ldb + k])
@@ -66,17 +71,29 @@ def operand_matrices(a, b, layout, m, n, k, lda, ldb, batch_index, stride_a, str
     return am, bm
 
 
+def bias_values(bias, n, bias_fmt=None, bias_scale_inv=None):
+    """The bias as float64 values of float32 numbers: bf16 bits widened, or
+    8-bit codes (bias_fmt given) as fl32(dec(code) * bias_scale_inv)."""
+    if bias is None:
+        return np.zeros(n)
+    if bias_fmt is None:
+        return bf16_to_f32(np.asarray(bias, dtype=np.uint16)).astype(np.float64)
+    dec = decode_fp8(np.asarray(bias, dtype=np.uint8), bias_fmt).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        return (dec * np.float32(bias_scale_inv)).astype(np.float32).astype(np.float64)
+
+
 def mm(a, b, fmt_a, fmt_b, layout, m, n, k, lda, ldb, sa_inv, sb_inv,
-       bias=None, batch=1, stride_a=0, stride_b=0):
+       bias=None, batch=1, stride_a=0, stride_b=0, bias_fmt=None, bias_scale_inv=None):
     """Full result.  Returns (y float64 [batch, m, n], out bf16 bits [batch, m, n]).
 
     sa_inv / sb_inv are the float32 dequantization multipliers (the reciprocal
-    of the scale each operand was quantized with); bias is bf16 bits [n] or None.
+    of the scale each operand was quantized with); bias is bf16 bits [n], or
+    8-bit codes [n] with bias_fmt and bias_scale_inv, or None.
     """
     batch = max(int(batch), 1)
     y = np.zeros((batch, m, n), dtype=np.float64)
-    bias64 = (np.zeros(n) if bias is None
-              else bf16_to_f32(np.asarray(bias, dtype=np.uint16)).astype(np.float64))
+    bias64 = bias_values(bias, n, bias_fmt, bias_scale_inv)
     for bi in range(batch):
         am, bm = operand_matrices(a, b, layout, m, n, k, lda, ldb, bi, stride_a, stride_b)
         acc = decode_fp8(am, fmt_a) @ decode_fp8(bm, fmt_b) if k > 0 else np.zeros((m, n))
@@ -85,7 +102,7 @@ def mm(a, b, fmt_a, fmt_b, layout, m, n, k, lda, ldb, sa_inv, sb_inv,
 
 
 def mm_entries(a, b, fmt_a, fmt_b, layout, m, n, k, lda, ldb, sa_inv, sb_inv,
-               bi, mi, ni, bias=None, stride_a=0, stride_b=0):
+               bi, mi, ni, bias=None, stride_a=0, stride_b=0, bias_fmt=None, bias_scale_inv=None):
     """Selected entries (bi[t], mi[t], ni[t]) of the same definition, one dot
     product each, for outputs too large to form whole."""
     a = np.asarray(a, dtype=np.uint8).reshape(-1)
@@ -106,7 +123,7 @@ def mm_entries(a, b, fmt_a, fmt_b, layout, m, n, k, lda, ldb, sa_inv, sb_inv,
         ib = base_b + kk * ldb + ni[:, None]
     acc = (decode_fp8(a[ia], fmt_a) * decode_fp8(b[ib], fmt_b)).sum(axis=1)
     bias64 = (np.zeros(len(ni)) if bias is None else
-              bf16_to_f32(np.asarray(bias, dtype=np.uint16)[ni]).astype(np.float64))
+              bias_values(np.asarray(bias)[ni], len(ni), bias_fmt, bias_scale_inv))
     y = acc * np.float64(np.float32(sa_inv)) * np.float64(np.float32(sb_inv)) + bias64
     return y, f64_to_bf16(y)
 
@@ -129,4 +146,4 @@ def max_abs_dequant(codes, fmt, s_inv):
 
 
 __all__ = ["NT", "NN", "TN", "mm", "mm_entries", "tolerance", "operand_matrices",
-           "max_abs_dequant"]
+           "max_abs_dequant", "bias_values"]

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from .formats import E4M3, E5M2, FMAX, bf16_to_f32, encode_fp8
+from .formats import E4M3, E5M2, FMAX, IN_BF16, encode_fp8, input_to_f32
 
 
 @dataclass
@@ -62,25 +62,26 @@ def ring_init(hist_len, fmt, init_scale=1.0):
                 np.zeros(hist_len, dtype=np.float32))
 
 
-def amax(x_bf16):
+def amax(x_bits, kind=IN_BF16):
     """max |x| over the tensor, taken on the float32 bit patterns of |x|.
 
     |x| as float32 is non-negative, so its bit pattern orders like its value,
-    with any NaN above +inf.  Exact and independent of order.
+    with any NaN above +inf.  Exact and independent of order.  x holds raw
+    bits of the input type `kind` (bf16 by default).
     """
-    x = np.asarray(x_bf16, dtype=np.uint16).reshape(-1)
+    x = np.asarray(x_bits).reshape(-1)
     if x.size == 0:
         return np.float32(0.0)
-    mag_bits = bf16_to_f32(x).view(np.uint32) & np.uint32(0x7FFFFFFF)
+    mag_bits = input_to_f32(x, kind).view(np.uint32) & np.uint32(0x7FFFFFFF)
     return np.uint32(mag_bits.max()).view(np.float32)
 
 
-def quantize_values(x_bf16, scale, fmt):
+def quantize_values(x_bits, scale, fmt, kind=IN_BF16):
     """Codes of cast(fl32(x) * scale): one float32 multiply, then encode.
 
     A NaN element keeps the sign of the input element.
     """
-    x = bf16_to_f32(np.asarray(x_bf16, dtype=np.uint16))
+    x = input_to_f32(np.asarray(x_bits), kind)
     with np.errstate(over="ignore", invalid="ignore"):
         v = x * np.float32(scale)                 # IEEE binary32 product, nearest-even
     v = np.where(np.isnan(x), np.copysign(np.float32(np.nan), x), v).astype(np.float32)
@@ -111,17 +112,17 @@ def advance_ring(ring, a):
     return r
 
 
-def quantize_step(ring, x_bf16):
+def quantize_step(ring, x_bits, kind=IN_BF16):
     """One delayed-scaling quantize call.
 
     Returns (codes, new ring).  In order: quantize with the current scale,
     then advance the ring with the tensor's amax (advance_ring).
     """
-    x = np.asarray(x_bf16, dtype=np.uint16)
+    x = np.asarray(x_bits)
     if x.size == 0:
         return np.zeros(x.shape, dtype=np.uint8), ring.copy()
-    codes = quantize_values(x, np.float32(ring.scale), ring.fmt)
-    return codes, advance_ring(ring, amax(x))
+    codes = quantize_values(x, np.float32(ring.scale), ring.fmt, kind)
+    return codes, advance_ring(ring, amax(x, kind))
 
 
 __all__ = ["Ring", "ring_init", "amax", "quantize_values", "next_scale", "advance_ring",
