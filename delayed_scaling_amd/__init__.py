@@ -9,9 +9,13 @@ fallback.
 Entry points (same names as the C ABI in include/fp8ds.h):
     scale_ring_bytes(hist_len)
     scale_ring_init(ring, hist_len, fmt, init_scale=1.0)
-    fp8_quantize(x_bf16, fmt, ring, out=None)
+    fp8_quantize(x, fmt, ring, out=None)             bf16 / fp16 / fp32 x
+    fp8_quantize_2d(x, fmt, ring, layout, ...)       row-wise, transposed, dual
+    fp8_quantize_dynamic(x, fmt, ring, out=None)     scale from x's own amax
+    fp8_bias_grad(g, ..., out=None)                  column sums of a gradient
     fp8_mm(a, b, ..., out=None)
-plus ScaleRing (a ring in a torch uint8 device tensor) and read_ring().
+plus ScaleRing (a ring in a torch uint8 device tensor), BiasGradWorkspace and
+read_ring().
 """
 import ctypes
 import os
@@ -22,7 +26,11 @@ import torch
 E4M3 = 0
 E5M2 = 1
 NT, NN, TN = 0, 1, 2
-BIAS_NONE, BIAS_BF16, BIAS_F32 = 0, 1, 2
+BIAS_NONE, BIAS_BF16, BIAS_F32, BIAS_E4M3, BIAS_E5M2 = 0, 1, 2, 3, 4
+IN_BF16, IN_F16, IN_F32 = 0, 1, 2
+ROWWISE, TRANSPOSED, DUAL = 0, 1, 2
+G_BF16, G_F16, G_F32, G_E4M3, G_E5M2 = 0, 1, 2, 3, 4
+_IN_TYPE = {torch.bfloat16: IN_BF16, torch.float16: IN_F16, torch.float32: IN_F32}
 TILES = {"256x256": 0, "128x128": 1, "64x64": 2, "256x128": 3, "128x256": 4, "256x256w8n": 5, "256x256w8": 6}
 RING_HIST_OFFSET = 2112   # byte offset of hist[] in a ring (include/fp8ds.h)
 RING_GROUPS = 32          # completion-tree scratch lines after the 64-byte header
@@ -44,6 +52,7 @@ class _MmArgs(ctypes.Structure):
         ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64),
         ("stride_a", ctypes.c_int64), ("stride_b", ctypes.c_int64), ("stride_c", ctypes.c_int64),
         ("a_scale_inv", ctypes.c_void_p), ("b_scale_inv", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("bias_scale_inv", ctypes.c_void_p),
     ]
 
 
@@ -73,6 +82,17 @@ def lib():
         L.fp8_mm_with_tile.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm_with_grid.restype = ctypes.c_int
         L.fp8_mm_with_grid.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.fp8_quantize_ex.restype = i32
+        L.fp8_quantize_ex.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.fp8_quantize_2d.restype = i32
+        L.fp8_quantize_2d.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+        L.fp8_quantize_dynamic.restype = i32
+        L.fp8_quantize_dynamic.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.fp8_bias_grad_workspace_bytes.restype = ctypes.c_size_t
+        L.fp8_bias_grad_workspace_bytes.argtypes = [i64, i64]
+        L.fp8_bias_grad.restype = i32
+        L.fp8_bias_grad.argtypes = [vp, i64, i64, i32, vp, i32, vp, vp, vp]
         L.fp8_last_error.restype = ctypes.c_char_p
         L.fp8_last_error.argtypes = []
         _lib = L
@@ -138,18 +158,99 @@ def read_ring(buf):
             "amax_last_bits": struct.unpack_from("<I", raw, 8)[0]}
 
 
+def _in_type(x):
+    t = _IN_TYPE.get(x.dtype)
+    if t is None or not x.is_cuda or not x.is_contiguous():
+        raise Fp8dsError("x must be a contiguous bf16, fp16 or fp32 CUDA tensor")
+    return t
+
+
+def _ring_buf(ring):
+    return ring.buf if isinstance(ring, ScaleRing) else ring
+
+
 def fp8_quantize(x, fmt, ring, out=None, stream=None, max_blocks=None):
-    """Quantize bf16 tensor x with the ring's scale into uint8 codes; advances the ring."""
-    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
-        raise Fp8dsError("x must be a contiguous bf16 CUDA tensor")
+    """Quantize x (bf16, fp16 or fp32) with the ring's scale into uint8 codes;
+    advances the ring."""
+    in_type = _in_type(x)
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    rbuf = ring.buf if isinstance(ring, ScaleRing) else ring
-    if max_blocks is None:
-        _check(lib().fp8_quantize(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out), _stream(stream)))
-    else:
+    rbuf = _ring_buf(ring)
+    if max_blocks is not None:
+        if in_type != IN_BF16:
+            raise Fp8dsError("max_blocks is available for bf16 inputs")
         _check(lib().fp8_quantize_with_grid(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out),
                                             int(max_blocks), _stream(stream)))
+    elif in_type == IN_BF16:
+        _check(lib().fp8_quantize(_ptr(x), x.numel(), int(fmt), _ptr(rbuf), _ptr(out), _stream(stream)))
+    else:
+        _check(lib().fp8_quantize_ex(_ptr(x), x.numel(), in_type, int(fmt), _ptr(rbuf), _ptr(out),
+                                     _stream(stream)))
+    return out
+
+
+def fp8_quantize_2d(x, fmt, ring, layout, out=None, out_t=None, stream=None):
+    """Quantize a 2-D tensor x [R, C] row-wise, transposed (codes of x.T, [C, R])
+    or both (DUAL).  Returns (out, out_t), None for the orientation not made."""
+    in_type = _in_type(x)
+    if x.dim() != 2:
+        raise Fp8dsError("x must be 2-D")
+    rows, cols = x.shape
+    if layout in (ROWWISE, DUAL) and out is None:
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if layout in (TRANSPOSED, DUAL) and out_t is None:
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_quantize_2d(_ptr(x), rows, cols, in_type, int(fmt), int(layout), _ptr(_ring_buf(ring)),
+                                 _ptr(out) if layout != TRANSPOSED else None,
+                                 _ptr(out_t) if layout != ROWWISE else None, _stream(stream)))
+    return (out if layout != TRANSPOSED else None), (out_t if layout != ROWWISE else None)
+
+
+def fp8_quantize_dynamic(x, fmt, ring, out=None, stream=None):
+    """Dynamic scaling: quantize x with FMAX / amax(x); ring must have hist_len 1
+    and afterwards holds scale_inv_used for the GEMM."""
+    in_type = _in_type(x)
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().fp8_quantize_dynamic(_ptr(x), x.numel(), in_type, int(fmt), _ptr(_ring_buf(ring)), _ptr(out),
+                                      _stream(stream)))
+    return out
+
+
+def bias_grad_workspace_bytes(rows, cols):
+    return int(lib().fp8_bias_grad_workspace_bytes(int(rows), int(cols)))
+
+
+class BiasGradWorkspace:
+    """Zero-filled device workspace for fp8_bias_grad on [rows, cols] gradients."""
+
+    def __init__(self, rows, cols, device="cuda"):
+        self.shape = (int(rows), int(cols))
+        self.buf = torch.zeros(max(bias_grad_workspace_bytes(rows, cols), 16), dtype=torch.uint8, device=device)
+
+
+def fp8_bias_grad(g, rows=None, cols=None, fmt=None, g_scale_inv=None, out_f32=False, out=None,
+                  workspace=None, stream=None):
+    """Column sums of the gradient g [rows, cols]: bf16 / fp16 / fp32 tensors, or
+    uint8 codes of format fmt dequantized with g_scale_inv (ScaleRing, fp32
+    device tensor or address).  Returns bf16 [cols] (fp32 with out_f32)."""
+    if g.dim() == 2 and rows is None:
+        rows, cols = g.shape
+    if g.dtype == torch.uint8:
+        if fmt is None:
+            raise Fp8dsError("uint8 gradients need fmt")
+        g_type = G_E4M3 if int(fmt) == E4M3 else G_E5M2
+    else:
+        g_type = {torch.bfloat16: G_BF16, torch.float16: G_F16, torch.float32: G_F32}.get(g.dtype)
+        if g_type is None:
+            raise Fp8dsError("g must be bf16, fp16, fp32 or uint8 codes")
+    if out is None:
+        out = torch.empty(int(cols), dtype=torch.float32 if out_f32 else torch.bfloat16, device=g.device)
+    if workspace is None:
+        workspace = BiasGradWorkspace(rows, cols, g.device)
+    wbuf = workspace.buf if isinstance(workspace, BiasGradWorkspace) else workspace
+    _check(lib().fp8_bias_grad(_ptr(g), int(rows), int(cols), g_type, _addr(g_scale_inv), int(bool(out_f32)),
+                               _ptr(out), _ptr(wbuf), _stream(stream)))
     return out
 
 
@@ -165,7 +266,7 @@ def _addr(x):
 
 def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
            batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
-           tile=None, max_workgroups=None, stream=None):
+           tile=None, max_workgroups=None, bias_fmt=None, bias_scale_inv=None, stream=None):
     """C = bf16(A @ B * a_scale_inv * b_scale_inv + bias) on uint8 fp8 code tensors.
 
     a, b: uint8 device tensors holding the stored operands (see include/fp8ds.h
@@ -190,13 +291,18 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
         out = torch.empty(batch * stride_c if batch > 1 else m * ldc, dtype=torch.bfloat16, device=dev)
     bias_kind = BIAS_NONE
     if bias is not None:
-        bias_kind = {torch.bfloat16: BIAS_BF16, torch.float32: BIAS_F32}.get(bias.dtype)
+        if bias.dtype == torch.uint8:
+            if bias_fmt is None or bias_scale_inv is None:
+                raise Fp8dsError("an 8-bit bias needs bias_fmt and bias_scale_inv")
+            bias_kind = BIAS_E4M3 if int(bias_fmt) == E4M3 else BIAS_E5M2
+        else:
+            bias_kind = {torch.bfloat16: BIAS_BF16, torch.float32: BIAS_F32}.get(bias.dtype)
         if bias_kind is None:
-            raise Fp8dsError("bias must be bf16 or fp32")
+            raise Fp8dsError("bias must be bf16, fp32 or uint8 codes")
     args = _MmArgs(_addr(a), _addr(b), _addr(out), int(fmt_a), int(fmt_b), int(layout), bias_kind,
                    int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
                    int(stride_a), int(stride_b), int(stride_c),
-                   _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias))
+                   _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias), _addr(bias_scale_inv))
     if tile is None and max_workgroups is None:
         _check(lib().fp8_mm(ctypes.byref(args), _stream(stream)))
     else:
@@ -206,4 +312,6 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
 
 
 __all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm",
-           "fp8_quantize", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH"]
+           "fp8_quantize", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad", "BiasGradWorkspace",
+           "bias_grad_workspace_bytes", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH",
+           "IN_BF16", "IN_F16", "IN_F32", "ROWWISE", "TRANSPOSED", "DUAL"]

@@ -31,6 +31,29 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_fmt(int f) { return f == FP8DS_E4M3 || f == FP8DS_E5M2; }
+bool valid_in(int t) { return t == FP8DS_IN_BF16 || t == FP8DS_IN_F16 || t == FP8DS_IN_F32; }
+int64_t in_size(int t) { return t == FP8DS_IN_F32 ? 4 : 2; }
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
+}
+
+// Checks shared by the 1-D quantize entry points; FP8DS_OK when launchable.
+int check_quantize(const char* fn, const void* x, int64_t numel, int in_type, int fmt, const void* ring,
+                   const void* y, int max_blocks) {
+  if (max_blocks < 0 || max_blocks > (1 << 20))
+    return set_error(FP8DS_EINVAL, "%s: max_blocks %d outside [0, 2^20]", fn, max_blocks);
+  if (!valid_in(in_type)) return set_error(FP8DS_EINVAL, "%s: in_type %d is not bf16 (0), fp16 (1) or fp32 (2)", fn, in_type);
+  if (!valid_fmt(fmt)) return set_error(FP8DS_EINVAL, "%s: fmt %d is neither E4M3 (0) nor E5M2 (1)", fn, fmt);
+  if (numel < 0) return set_error(FP8DS_EINVAL, "%s: numel %lld < 0", fn, (long long)numel);
+  if (!ring) return set_error(FP8DS_EUNSUPPORTED, "%s: ring is NULL (use fp8_quantize_dynamic for dynamic scaling)", fn);
+  if (!aligned16(ring)) return set_error(FP8DS_EALIGN, "%s: ring not 16-byte aligned", fn);
+  if (numel == 0) return FP8DS_OK;
+  if (!x || !y) return set_error(FP8DS_EINVAL, "%s: x or y is NULL", fn);
+  if (!aligned16(x) || !aligned16(y)) return set_error(FP8DS_EALIGN, "%s: x or y not 16-byte aligned", fn);
+  if (overlaps(x, numel * in_size(in_type), y, numel)) return set_error(FP8DS_EINVAL, "%s: x and y overlap", fn);
+  return FP8DS_OK;
+}
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 
 // Largest byte offset + 1 that one batch entry of a stored [rows][cols] view
@@ -76,19 +99,76 @@ int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y
 
 int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, int max_blocks,
                            void* stream) {
-  if (max_blocks < 0 || max_blocks > (1 << 20))
-    return set_error(FP8DS_EINVAL, "fp8_quantize: max_blocks %d outside [0, 2^20]", max_blocks);
-  if (!valid_fmt(fmt)) return set_error(FP8DS_EINVAL, "fp8_quantize: fmt %d is neither E4M3 (0) nor E5M2 (1)", fmt);
-  if (numel < 0) return set_error(FP8DS_EINVAL, "fp8_quantize: numel %lld < 0", (long long)numel);
-  if (!ring) return set_error(FP8DS_EUNSUPPORTED, "fp8_quantize: ring is NULL (dynamic scaling is not provided)");
-  if (!aligned16(ring)) return set_error(FP8DS_EALIGN, "fp8_quantize: ring not 16-byte aligned");
-  if (numel == 0) return FP8DS_OK;
-  if (!x_bf16 || !y_fp8) return set_error(FP8DS_EINVAL, "fp8_quantize: x or y is NULL");
-  if (!aligned16(x_bf16) || !aligned16(y_fp8)) return set_error(FP8DS_EALIGN, "fp8_quantize: x or y not 16-byte aligned");
-  const uintptr_t xs = reinterpret_cast<uintptr_t>(x_bf16), ys = reinterpret_cast<uintptr_t>(y_fp8);
-  if (xs < ys + (uintptr_t)numel && ys < xs + 2 * (uintptr_t)numel)
-    return set_error(FP8DS_EINVAL, "fp8_quantize: x and y overlap");
-  return launch_quantize(x_bf16, numel, fmt, ring, y_fp8, max_blocks, static_cast<hipStream_t>(stream));
+  const int st = check_quantize("fp8_quantize", x_bf16, numel, FP8DS_IN_BF16, fmt, ring, y_fp8, max_blocks);
+  if (st != FP8DS_OK || numel == 0) return st;
+  return launch_quantize(x_bf16, numel, FP8DS_IN_BF16, fmt, ring, y_fp8, max_blocks, static_cast<hipStream_t>(stream));
+}
+
+int fp8_quantize_ex(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream) {
+  const int st = check_quantize("fp8_quantize_ex", x, numel, in_type, fmt, ring, y_fp8, 0);
+  if (st != FP8DS_OK || numel == 0) return st;
+  return launch_quantize(x, numel, in_type, fmt, ring, y_fp8, 0, static_cast<hipStream_t>(stream));
+}
+
+int fp8_quantize_dynamic(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream) {
+  const int st = check_quantize("fp8_quantize_dynamic", x, numel, in_type, fmt, ring, y_fp8, 0);
+  if (st != FP8DS_OK || numel == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int a = launch_amax(x, numel, in_type, fmt, ring, s);
+  if (a != FP8DS_OK) return a;
+  return launch_quantize(x, numel, in_type, fmt, ring, y_fp8, 0, s);
+}
+
+int fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, int in_type, int fmt, int layout, void* ring, void* y,
+                    void* y_t, void* stream) {
+  const char* fn = "fp8_quantize_2d";
+  if (layout < FP8DS_ROWWISE || layout > FP8DS_DUAL) return set_error(FP8DS_EINVAL, "%s: bad layout %d", fn, layout);
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+    return set_error(FP8DS_EINVAL, "%s: rows and cols must be in [0, 2^31)", fn);
+  const int64_t numel = rows * cols;
+  if (layout == FP8DS_ROWWISE) {
+    const int st = check_quantize(fn, x, numel, in_type, fmt, ring, y, 0);
+    if (st != FP8DS_OK || numel == 0) return st;
+    return launch_quantize(x, numel, in_type, fmt, ring, y, 0, static_cast<hipStream_t>(stream));
+  }
+  const bool dual = layout == FP8DS_DUAL;
+  const int st = check_quantize(fn, x, numel, in_type, fmt, ring, y_t, 0);
+  if (st != FP8DS_OK || numel == 0) return st;
+  if ((rows & 15) || (cols & 15))
+    return set_error(FP8DS_EALIGN, "%s: transposed forms need rows and cols multiples of 16 (got %lld x %lld)", fn,
+                     (long long)rows, (long long)cols);
+  if (dual) {
+    if (!y) return set_error(FP8DS_EINVAL, "%s: DUAL needs y", fn);
+    if (!aligned16(y)) return set_error(FP8DS_EALIGN, "%s: y not 16-byte aligned", fn);
+    if (overlaps(x, numel * in_size(in_type), y, numel) || overlaps(y, numel, y_t, numel))
+      return set_error(FP8DS_EINVAL, "%s: y overlaps x or y_t", fn);
+  }
+  return launch_quantize_2d(x, (int)rows, (int)cols, in_type, fmt, dual, ring, y, y_t, 0,
+                            static_cast<hipStream_t>(stream));
+}
+
+size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || rows > kMaxDim || cols > kMaxDim) return 0;
+  return bias_grad_workspace(rows, cols);
+}
+
+int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv, int out_f32,
+                  void* out, void* workspace, void* stream) {
+  const char* fn = "fp8_bias_grad";
+  if (g_type < FP8DS_G_BF16 || g_type > FP8DS_G_E5M2) return set_error(FP8DS_EINVAL, "%s: bad g_type %d", fn, g_type);
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+    return set_error(FP8DS_EINVAL, "%s: rows and cols must be in [0, 2^31)", fn);
+  if (cols == 0) return FP8DS_OK;
+  if (!out || !workspace || (rows > 0 && !g)) return set_error(FP8DS_EINVAL, "%s: g, out or workspace is NULL", fn);
+  const bool codes = g_type == FP8DS_G_E4M3 || g_type == FP8DS_G_E5M2;
+  if (codes && !g_scale_inv) return set_error(FP8DS_EINVAL, "%s: 8-bit g needs g_scale_inv", fn);
+  if (cols & 7) return set_error(FP8DS_EALIGN, "%s: cols %lld is not a multiple of 8", fn, (long long)cols);
+  if ((rows > 0 && !aligned16(g)) || !aligned16(workspace))
+    return set_error(FP8DS_EALIGN, "%s: g or workspace not 16-byte aligned", fn);
+  const int64_t esize = g_type == FP8DS_G_F32 ? 4 : codes ? 1 : 2;
+  if (rows * cols * esize >= (int64_t)1 << 40) return set_error(FP8DS_EUNSUPPORTED, "%s: g too large", fn);
+  return launch_bias_grad(g, (int)rows, (int)cols, g_type, g_scale_inv, out_f32 != 0, out, workspace,
+                          static_cast<hipStream_t>(stream));
 }
 
 int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_grid(a, -1, 0, stream); }
@@ -100,8 +180,10 @@ int fp8_mm_with_grid(const fp8_mm_args* a, int tile, int max_workgroups, void* s
   if (max_workgroups < 0) return set_error(FP8DS_EINVAL, "fp8_mm: max_workgroups %d < 0", max_workgroups);
   if (!valid_fmt(a->fmt_a) || !valid_fmt(a->fmt_b)) return set_error(FP8DS_EINVAL, "fp8_mm: bad fmt_a/fmt_b");
   if (a->layout < FP8DS_NT || a->layout > FP8DS_TN) return set_error(FP8DS_EINVAL, "fp8_mm: bad layout %d", a->layout);
-  if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_F32)
+  if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_E5M2)
     return set_error(FP8DS_EINVAL, "fp8_mm: bad bias_kind %d", a->bias_kind);
+  if ((a->bias_kind == FP8DS_BIAS_E4M3 || a->bias_kind == FP8DS_BIAS_E5M2) && !a->bias_scale_inv)
+    return set_error(FP8DS_EINVAL, "fp8_mm: an 8-bit bias needs bias_scale_inv");
   const int64_t m = a->m, n = a->n, k = a->k, batch = a->batch == 0 ? 1 : a->batch;
   if (m < 0 || n < 0 || k < 0 || batch < 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || batch > kMaxDim)
     return set_error(FP8DS_EINVAL, "fp8_mm: dimensions must be in [0, 2^31)");
@@ -149,6 +231,7 @@ int fp8_mm_with_grid(const fp8_mm_args* a, int tile, int max_workgroups, void* s
   p.a_scale_inv = a->a_scale_inv;
   p.b_scale_inv = a->b_scale_inv;
   p.bias = a->bias;
+  p.bias_scale_inv = a->bias_scale_inv;
   return launch_gemm(p, tile, max_workgroups, static_cast<hipStream_t>(stream));
 }
 

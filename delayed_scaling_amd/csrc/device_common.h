@@ -20,6 +20,11 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 constexpr int kE4M3 = 0;
 constexpr int kE5M2 = 1;
 
+// Quantize input element types (fp8ds_in_type).
+constexpr int kInBf16 = 0;
+constexpr int kInF16 = 1;
+constexpr int kInF32 = 2;
+
 // Byte layout of the scale ring (documented in include/fp8ds.h).
 struct RingHeader {
   float scale;

@@ -58,6 +58,7 @@ struct GemmKArgs {
   const float* a_scale_inv;
   const float* b_scale_inv;
   const void* bias;
+  const float* bias_scale_inv;
   int bias_kind;
   int ldc_small;   // 256 * ldc < 2^31: offsets inside a tile fit 32 bits
 };
@@ -275,6 +276,18 @@ __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&ac
         } else {
           for (int e = 0; e < 4; ++e)
             if (n + e < p.n) bias4[e] = bp[e];
+        }
+      } else if (p.bias_kind >= 3) {
+        // 8-bit bias: fl32(dec(code) * bias_scale_inv), after the operand scaling.
+        const uint8_t* bp = static_cast<const uint8_t*>(p.bias) + n;
+        const float bsi = p.bias_scale_inv[0];
+        uint32_t w = 0;
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.n) w |= (uint32_t)bp[e] << (8 * e);
+        for (int e = 0; e < 4; ++e) {
+          const int c = (int)(w >> (8 * e));
+          const float d = p.bias_kind == 3 ? __builtin_amdgcn_cvt_f32_fp8(c, 0) : __builtin_amdgcn_cvt_f32_bf8(c, 0);
+          bias4[e] = d * bsi;
         }
       }
 #pragma unroll
@@ -687,6 +700,7 @@ int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hip
   k.a_scale_inv = p.a_scale_inv;
   k.b_scale_inv = p.b_scale_inv;
   k.bias = p.bias;
+  k.bias_scale_inv = p.bias_scale_inv;
   k.bias_kind = p.bias_kind;
   k.ldc_small = p.ldc * 256 < 0x80000000LL;
   const int64_t total = (int64_t)k.tiles_m * k.tiles_n * k.batch;

@@ -13,7 +13,14 @@ int set_error(int code, const char* fmt, ...);
 int check_launch(const char* kernel_name);
 
 int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStream_t stream);
-int launch_quantize(const void* x, int64_t numel, int fmt, void* ring, void* y, int max_blocks, hipStream_t stream);
+int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y, int max_blocks,
+                    hipStream_t stream);
+int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, bool dual, void* ring, void* y,
+                       void* y_t, int max_blocks, hipStream_t stream);
+int launch_amax(const void* x, int64_t numel, int in_type, int fmt, void* ring, hipStream_t stream);
+size_t bias_grad_workspace(int64_t rows, int64_t cols);
+int launch_bias_grad(const void* g, int rows, int cols, int g_type, const float* g_scale_inv, int out_f32, void* out,
+                     void* workspace, hipStream_t stream);
 
 struct GemmProblem {
   const uint8_t* a;
@@ -27,6 +34,7 @@ struct GemmProblem {
   const float* a_scale_inv;
   const float* b_scale_inv;
   const void* bias;
+  const float* bias_scale_inv;   // 8-bit bias only
 };
 
 // tile_override < 0 picks the tile; max_workgroups <= 0 sizes the grid to the

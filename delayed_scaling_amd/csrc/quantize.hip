@@ -1,15 +1,24 @@
-// Delayed-scaling bf16 -> FP8 quantize with a fused amax and an in-kernel
-// scale-ring update (AstrAI history of astrai/extension/fp8.py @4dc5e923,
-// ring-finalize entry: the last block to finish folds the amax into the
-// history, reduces the window and publishes the next scale, so the update
-// costs no extra launch).
+// Delayed-scaling FP8 quantize with a fused amax and an in-kernel scale-ring
+// update, its transposed / dual form, the dynamic recipe's amax pass and the
+// bias-gradient column sum.
 //
-// One launch streams x once (16-byte loads, 8-byte stores), so the kernel is
-// bound by HBM: 3 bytes per element.  Each block reduces max|x| over its
-// elements and climbs a two-level completion tree kept in the ring's scratch
-// lines (per-group max + ticket, then a top-level max + ticket); the block
-// holding the last top-level ticket finalizes the ring and every scratch
-// word is back at zero for the next call on the same stream.
+// Pages (AstrAI commit histories):
+//  * astrai/extension/fp8.py @4dc5e923, ring-finalize entry: the last block
+//    to finish folds the amax into the history, reduces the window and
+//    publishes the next scale, so the update costs no extra launch;
+//  * fp8.py @f4c44ebf: the quantize is templated on its input type (bf16,
+//    fp16, fp32); the bias gradient is a column sum taken only when needed,
+//    over a dequantized gradient when the gradient is pre-quantized;
+//  * history of `tests`: quantize and quantize_dual with a layout enum, the
+//    two orientations byte-equal to the plain one;
+//  * fp8.py @4dc5e923: the dynamic recipe measures its scale inline.
+//
+// Each quantize launch streams x once (16-byte loads), so the kernels are
+// bound by HBM.  Each block reduces max|x| over its elements and climbs a
+// two-level completion tree kept in the ring's scratch lines (per-group max +
+// ticket, then a top-level max + ticket); the block holding the last
+// top-level ticket finalizes the ring and every scratch word is back at zero
+// for the next call on the same stream.
 #include "device_common.h"
 #include "launch.h"
 
@@ -20,6 +29,43 @@ namespace {
 constexpr int kQBlock = 256;     // threads per block
 constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
 constexpr int kDefaultBlocks = 1024;  // grid cap: 4 blocks per CU; larger inputs loop
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// Element types.  mag() is a bit pattern of |x| that orders like |x| (NaN
+// above infinity); mag_f32() turns the largest one into float32 bits.
+
+template <int IN>
+struct In;
+template <>
+struct In<kInBf16> {
+  static constexpr int kBits = 16;
+  static constexpr uint32_t kInfMag = 0x7F80u;
+  __device__ static float f(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static uint32_t mag(uint32_t b) { return b & 0x7FFFu; }
+  __device__ static uint32_t mag_f32(uint32_t m) { return m << 16; }
+  __device__ static uint32_t sign(uint32_t b) { return (b >> 8) & 0x80u; }
+};
+template <>
+struct In<kInF16> {
+  static constexpr int kBits = 16;
+  static constexpr uint32_t kInfMag = 0x7C00u;
+  __device__ static float f(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+  __device__ static uint32_t mag(uint32_t b) { return b & 0x7FFFu; }
+  __device__ static uint32_t mag_f32(uint32_t m) { return __float_as_uint(f(m)); }
+  __device__ static uint32_t sign(uint32_t b) { return (b >> 8) & 0x80u; }
+};
+template <>
+struct In<kInF32> {
+  static constexpr int kBits = 32;
+  static constexpr uint32_t kInfMag = 0x7F800000u;
+  __device__ static float f(uint32_t b) { return __uint_as_float(b); }
+  __device__ static uint32_t mag(uint32_t b) { return b & 0x7FFFFFFFu; }
+  __device__ static uint32_t mag_f32(uint32_t m) { return m; }
+  __device__ static uint32_t sign(uint32_t b) { return (b >> 24) & 0x80u; }
+};
 
 // Casts two products to the format's codes in the low or high half-word of
 // `word`.  Products are clamped to +-FMAX first because the hardware convert
@@ -38,46 +84,35 @@ __device__ __forceinline__ float clamp_fmax(float v) {
   return fminf(fmaxf(v, -m), m);
 }
 
-// Quantizes 4 bf16 held in two 32-bit words into 4 codes packed in one word.
-template <int FMT>
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
-  const float f0 = __uint_as_float(w0 << 16), f1 = __uint_as_float(w0 & 0xFFFF0000u);
-  const float f2 = __uint_as_float(w1 << 16), f3 = __uint_as_float(w1 & 0xFFFF0000u);
-  const uint32_t out = cvt_pair<FMT, false>(clamp_fmax<FMT>(f0 * scale), clamp_fmax<FMT>(f1 * scale), 0u);
-  return cvt_pair<FMT, true>(clamp_fmax<FMT>(f2 * scale), clamp_fmax<FMT>(f3 * scale), out);
-}
-
-// A NaN element encodes as 0x7F with its sign; only chunks holding a NaN
-// take this path.
-__device__ __forceinline__ uint32_t fix_nan4(uint32_t w0, uint32_t w1, uint32_t codes) {
-  const uint32_t h[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+// Four elements (raw bits) to four codes packed in one word, NaN included:
+// a NaN element encodes as 0x7F with its sign.  amag collects max mag().
+template <int FMT, int IN>
+__device__ __forceinline__ uint32_t quant4(const uint32_t (&e)[4], float scale, uint32_t& amag) {
+  using T = In<IN>;
+  const uint32_t m = max(max(T::mag(e[0]), T::mag(e[1])), max(T::mag(e[2]), T::mag(e[3])));
+  amag = max(amag, m);
+  uint32_t out = cvt_pair<FMT, false>(clamp_fmax<FMT>(T::f(e[0]) * scale), clamp_fmax<FMT>(T::f(e[1]) * scale), 0u);
+  out = cvt_pair<FMT, true>(clamp_fmax<FMT>(T::f(e[2]) * scale), clamp_fmax<FMT>(T::f(e[3]) * scale), out);
+  if (m > T::kInfMag) {               // only chunks holding a NaN take this path
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if ((h[i] & 0x7FFFu) > 0x7F80u) {
-      const uint32_t code = 0x7Fu | ((h[i] >> 8) & 0x80u);
-      codes = (codes & ~(0xFFu << (8 * i))) | (code << (8 * i));
-    }
+    for (int i = 0; i < 4; ++i)
+      if (T::mag(e[i]) > T::kInfMag) out = (out & ~(0xFFu << (8 * i))) | ((0x7Fu | T::sign(e[i])) << (8 * i));
   }
-  return codes;
+  return out;
 }
 
-__device__ __forceinline__ uint32_t max_mag16(uint32_t w) {
-  const uint32_t m = w & 0x7FFF7FFFu;
-  return max(m & 0xFFFFu, m >> 16);
-}
-
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
-
-template <int FMT>
-__device__ __forceinline__ void quant_chunk(v4u v, float scale, v2u& out, uint32_t& amax16) {
-  const uint32_t cm = max(max(max_mag16(v.x), max_mag16(v.y)), max(max_mag16(v.z), max_mag16(v.w)));
-  amax16 = max(amax16, cm);
-  out.x = quant4<FMT>(v.x, v.y, scale);
-  out.y = quant4<FMT>(v.z, v.w, scale);
-  if (cm > 0x7F80u) {                 // a NaN is present in this chunk
-    out.x = fix_nan4(v.x, v.y, out.x);
-    out.y = fix_nan4(v.z, v.w, out.y);
+// 16 input bytes -> codes: 8 elements -> 2 words for 16-bit types, 4
+// elements -> 1 word for fp32.
+template <int FMT, int IN>
+__device__ __forceinline__ void quant16(v4u v, float scale, uint32_t (&out)[2], uint32_t& amag) {
+  if constexpr (In<IN>::kBits == 16) {
+    const uint32_t e0[4] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16};
+    const uint32_t e1[4] = {v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    out[0] = quant4<FMT, IN>(e0, scale, amag);
+    out[1] = quant4<FMT, IN>(e1, scale, amag);
+  } else {
+    const uint32_t e[4] = {v.x, v.y, v.z, v.w};
+    out[0] = quant4<FMT, IN>(e, scale, amag);
   }
 }
 
@@ -108,97 +143,69 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   return r;
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict__ x, v2u* __restrict__ y,
-                                                           int64_t nchunk, const uint16_t* __restrict__ x_tail,
-                                                           uint8_t* __restrict__ y_tail, int tail,
-                                                           RingHeader* __restrict__ ring) {
-  __shared__ uint32_t red[kQBlock / 64];
-  __shared__ int s_last;
-  const float scale = ring->scale;
-  uint32_t amax16 = 0;
+// Two-level completion tree, called by thread 0 of every block with the
+// block's max |x| as float32 bits.  Block b belongs to group b % kRingGroups;
+// each group has its own cache line holding a running max and a ticket.  All
+// words are device-scope atomics, performed where every XCD sees them.  A
+// ticket is taken only after the max it covers has been performed (its
+// returned value is waited for), so the block drawing a group's last ticket
+// reads a max that covers the whole group, and the block drawing the last
+// top-level ticket reads the max of all groups.  No release/acquire fence is
+// needed: nothing else a block wrote is read by the finalizing block, and an
+// agent-scope fence would write back the whole L2.  Returns true in exactly
+// one block, whose ring->amax_bits then holds the total.
+__device__ bool climb_tree(RingHeader* ring, uint32_t bmax) {
+  const int G = (int)gridDim.x;
+  const int ngroups = G < kRingGroups ? G : kRingGroups;
+  const int g = (int)blockIdx.x % kRingGroups;
+  const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);
+  RingGroup* grp = ring_groups(ring) + g;
+  const uint32_t prev = __hip_atomic_fetch_max(&grp->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(prev);
+  const uint32_t t = __hip_atomic_fetch_add(&grp->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(t);
+  if (t != members - 1) return false;
+  // Every member has performed its max and taken its ticket, so this block
+  // alone touches the group line now: read it, then clear it.  (Plain atomic
+  // loads and stores: an exchange whose returned value shared a register with
+  // its data was measured returning the new value on this target.)
+  const uint32_t gmax = __hip_atomic_load(&grp->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(gmax);
+  __hip_atomic_store(&grp->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&grp->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t prev2 = __hip_atomic_fetch_max(&ring->amax_bits, gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(prev2);
+  const uint32_t t2 = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(t2);
+  return t2 == (uint32_t)ngroups - 1;
+}
 
-  const int64_t step = (int64_t)gridDim.x * kQBlock * kQUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
-    if (base + (kQUnroll - 1) * kQBlock < nchunk) {
-      v4u v[kQUnroll];
-#pragma unroll
-      for (int u = 0; u < kQUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kQBlock);
-#pragma unroll
-      for (int u = 0; u < kQUnroll; ++u) {
-        v2u o;
-        quant_chunk<FMT>(v[u], scale, o, amax16);
-        __builtin_nontemporal_store(o, y + base + u * kQBlock);
-      }
-    } else {
-      for (int u = 0; u < kQUnroll; ++u) {
-        const int64_t c = base + u * kQBlock;
-        if (c < nchunk) {
-          v2u o;
-          quant_chunk<FMT>(x[c], scale, o, amax16);
-          y[c] = o;
-        }
-      }
-    }
-  }
-  // Elements past the last whole 8-element chunk.
-  if (tail > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
-    for (int i = 0; i < tail; ++i) {
-      const uint32_t h = x_tail[i];
-      amax16 = max(amax16, h & 0x7FFFu);
-      const float v = clamp_fmax<FMT>(__uint_as_float(h << 16) * scale);
-      uint32_t code = cvt_pair<FMT, false>(v, 0.0f, 0u) & 0xFFu;
-      if ((h & 0x7FFFu) > 0x7F80u) code = 0x7Fu | ((h >> 8) & 0x80u);
-      y_tail[i] = (uint8_t)code;
-    }
-  }
-
-  const uint32_t bmax = block_max(amax16, red) << 16;   // |x| as fp32 bits
-  if (threadIdx.x == 0) {
-    // Two-level completion tree.  Block b belongs to group b % kRingGroups;
-    // each group has its own cache line holding a running max and a ticket.
-    // All words are device-scope atomics, performed where every XCD sees
-    // them.  A ticket is taken only after the max it covers has been
-    // performed (its returned value is waited for), so the block drawing a
-    // group's last ticket reads a max that covers the whole group, and the
-    // block drawing the last top-level ticket reads the max of all groups.
-    // No release/acquire fence is needed: nothing else a block wrote is read
-    // by the finalizing block, and an agent-scope fence would write back the
-    // whole L2.
-    const int G = (int)gridDim.x;
-    const int ngroups = G < kRingGroups ? G : kRingGroups;
-    const int g = (int)blockIdx.x % kRingGroups;
-    const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);
-    RingGroup* grp = ring_groups(ring) + g;
-    const uint32_t prev = __hip_atomic_fetch_max(&grp->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_returned(prev);
-    const uint32_t t = __hip_atomic_fetch_add(&grp->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_returned(t);
-    int last = 0;
-    if (t == members - 1) {
-      // Every member has performed its max and taken its ticket, so this
-      // block alone touches the group line now: read it, then clear it.
-      // (Plain atomic loads and stores: an exchange whose returned value
-      // shared a register with its data was measured returning the new value
-      // on this target.)
-      const uint32_t gmax = __hip_atomic_load(&grp->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_returned(gmax);
-      __hip_atomic_store(&grp->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&grp->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t prev2 = __hip_atomic_fetch_max(&ring->amax_bits, gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_returned(prev2);
-      const uint32_t t2 = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_returned(t2);
-      last = t2 == (uint32_t)ngroups - 1;
-    }
-    s_last = last;
-  }
+// Reduces the block's max, climbs the tree and, in the one last block,
+// returns true with *a = max |x| of the whole launch (float32 bits).  The
+// caller finalizes the ring and then calls clear_top().
+__device__ __forceinline__ bool fold_amax(RingHeader* ring, uint32_t amag_f32, uint32_t* red, int* s_last,
+                                          uint32_t* a) {
+  const uint32_t bmax = block_max(amag_f32, red);
+  if (threadIdx.x == 0) *s_last = climb_tree(ring, bmax);
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_last) return false;
+  const uint32_t v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_returned(v);
+  *a = v;
+  return true;
+}
 
-  // Last block: fold, reduce the window, publish.
-  const uint32_t a = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_returned(a);
+__device__ __forceinline__ void clear_top(RingHeader* ring) {
+  __hip_atomic_store(&ring->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(&ring->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The delayed-scaling ring update, run by the last block with the launch's
+// amax a: hist[idx] = a, idx advances, the next scale is FMAX over the
+// window's max when that is finite and positive and the quotient finite,
+// scale_inv_used = 1/scale (the scale this launch applied), amax_last = a.
+template <int FMT>
+__device__ void finalize_ring(RingHeader* ring, uint32_t a, float scale, uint32_t* red) {
   const int H = ring->hist_len;
   const int idx = ring->idx;
   const bool bad_header = H < 1 || H > 1024 || idx < 0 || idx >= H;
@@ -224,9 +231,318 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
       ring->scale_inv_used = 1.0f / scale;
       ring->amax_last = __uint_as_float(a);
     }
-    __hip_atomic_store(&ring->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&ring->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    clear_top(ring);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise quantize: x is a flat array of numel elements.
+
+template <int FMT, int IN>
+__global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict__ x, uint8_t* __restrict__ y,
+                                                           int64_t nchunk, const uint8_t* __restrict__ x_tail,
+                                                           uint8_t* __restrict__ y_tail, int tail,
+                                                           RingHeader* __restrict__ ring) {
+  using T = In<IN>;
+  constexpr int kOut = T::kBits == 16 ? 8 : 4;   // codes per 16 input bytes
+  __shared__ uint32_t red[kQBlock / 64];
+  __shared__ int s_last;
+  const float scale = ring->scale;
+  uint32_t amag = 0;
+
+  auto put = [&](int64_t c, const uint32_t (&o)[2], bool stream) __attribute__((always_inline)) {
+    if constexpr (kOut == 8) {
+      v2u* p = reinterpret_cast<v2u*>(y) + c;
+      const v2u w = {o[0], o[1]};
+      if (stream) __builtin_nontemporal_store(w, p);
+      else *p = w;
+    } else {
+      uint32_t* p = reinterpret_cast<uint32_t*>(y) + c;
+      if (stream) __builtin_nontemporal_store(o[0], p);
+      else *p = o[0];
+    }
+  };
+  const int64_t step = (int64_t)gridDim.x * kQBlock * kQUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
+    if (base + (kQUnroll - 1) * kQBlock < nchunk) {
+      v4u v[kQUnroll];
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kQBlock);
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) {
+        uint32_t o[2];
+        quant16<FMT, IN>(v[u], scale, o, amag);
+        put(base + u * kQBlock, o, true);
+      }
+    } else {
+      for (int u = 0; u < kQUnroll; ++u) {
+        const int64_t c = base + u * kQBlock;
+        if (c < nchunk) {
+          uint32_t o[2];
+          quant16<FMT, IN>(x[c], scale, o, amag);
+          put(c, o, false);
+        }
+      }
+    }
+  }
+  // Elements past the last whole 16-byte chunk.
+  if (tail > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int i = 0; i < tail; ++i) {
+      uint32_t e[4] = {0u, 0u, 0u, 0u};
+      if constexpr (T::kBits == 16) e[0] = reinterpret_cast<const uint16_t*>(x_tail)[i];
+      else e[0] = reinterpret_cast<const uint32_t*>(x_tail)[i];
+      y_tail[i] = (uint8_t)(quant4<FMT, IN>(e, scale, amag) & 0xFFu);
+    }
+  }
+
+  uint32_t a;
+  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
+  finalize_ring<FMT>(ring, a, scale, red);
+}
+
+// ---------------------------------------------------------------------------
+// Transposed / dual quantize of an R x C row-major tensor, R and C multiples
+// of 16.  A block takes a 64 x 64 tile: each thread quantizes 16 consecutive
+// elements of one row (and, for the dual form, stores those 16 codes), then
+// writes them to an LDS tile [64 rows][64 codes] whose 16-byte chunks are
+// XOR-swizzled per row; transpose reads (ds_read_b64_tr_b8) hand each lane 16
+// consecutive rows of one column, stored as 16 bytes of the transposed output.
+
+constexpr int kTile = 64;
+
+__device__ __forceinline__ int tile_swz(int r) { return ((r >> 2) & 1) << 1; }
+
+template <int FMT, int IN, bool DUAL>
+__global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __restrict__ x, uint8_t* __restrict__ y,
+                                                              uint8_t* __restrict__ y_t, int rows, int cols,
+                                                              int tiles_c, RingHeader* __restrict__ ring) {
+  using T = In<IN>;
+  constexpr int kElemBytes = T::kBits / 8;
+  __shared__ __attribute__((aligned(16))) char codes_lds[kTile * kTile];
+  __shared__ uint32_t red[kQBlock / 64];
+  __shared__ int s_last;
+  const float scale = ring->scale;
+  uint32_t amag = 0;
+  lds_char_t* tile = (lds_char_t*)codes_lds;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tr = threadIdx.x >> 2, tch = threadIdx.x & 3;    // row in tile, 16-column chunk
+  const int ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int r0 = (t / tiles_c) * kTile, c0 = (t % tiles_c) * kTile;
+    const int r = r0 + tr, c = c0 + tch * 16;
+    const bool in = r < rows && c < cols;                     // cols % 16 == 0: whole chunk in or out
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (in) {
+      const v4u* src = reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes);
+      uint32_t o[2];
+      if constexpr (T::kBits == 16) {
+        quant16<FMT, IN>(__builtin_nontemporal_load(src), scale, o, amag);
+        w[0] = o[0]; w[1] = o[1];
+        quant16<FMT, IN>(__builtin_nontemporal_load(src + 1), scale, o, amag);
+        w[2] = o[0]; w[3] = o[1];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          quant16<FMT, IN>(__builtin_nontemporal_load(src + q), scale, o, amag);
+          w[q] = o[0];
+        }
+      }
+      if constexpr (DUAL)
+        __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u*>(y + (int64_t)r * cols + c));
+    }
+    __syncthreads();   // the previous tile's transpose reads are done
+    *(lds_v4i_t*)(tile + tr * kTile + ((tch ^ tile_swz(tr)) << 4)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    __syncthreads();
+    // Transposed store: lane l of wave w takes column c0 + 32*(w&1) + l%32
+    // and tile rows 32*(l/32) + 16*(w>>1) + [0, 16): two transpose reads of
+    // 8 rows each.
+    // Within each 16-lane group, the even lanes address rows k..k+7 of the
+    // group's first 8 columns and the odd lanes the next 8; a read hands each
+    // lane 8 consecutive rows of one column.
+    const int col = 32 * (wave & 1) + (lane & 31);
+    const int rbase = 32 * (lane >> 5) + 16 * (wave >> 1);
+    const int q = lane & 15;
+    const int chunk = 2 * (wave & 1) + ((lane >> 4) & 1);
+    v2i part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kr = rbase + 8 * h + (q >> 1);
+      const int addr = kr * kTile + ((chunk ^ tile_swz(kr)) << 4) + 8 * (q & 1);
+      part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(tile + addr));
+    }
+    const int oc = c0 + col, orow = r0 + rbase;
+    if (oc < cols && orow < rows)
+      __builtin_nontemporal_store(v4u{(uint32_t)part[0][0], (uint32_t)part[0][1], (uint32_t)part[1][0],
+                                      (uint32_t)part[1][1]},
+                                  reinterpret_cast<v4u*>(y_t + (int64_t)oc * rows + orow));
+  }
+
+  uint32_t a;
+  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
+  finalize_ring<FMT>(ring, a, scale, red);
+}
+
+// ---------------------------------------------------------------------------
+// Dynamic recipe, pass 1: max |x| over the tensor into a length-1 ring,
+// publishing scale = FMAX / amax (1 when amax is zero, infinite or NaN or the
+// quotient overflows).  The quantize pass that follows applies that scale and
+// folds the same amax again, which leaves the same scale and records
+// scale_inv_used = 1 / scale.
+
+template <int FMT, int IN>
+__global__ __launch_bounds__(kQBlock) void amax_kernel(const v4u* __restrict__ x, int64_t nchunk,
+                                                       const uint8_t* __restrict__ x_tail, int tail,
+                                                       RingHeader* __restrict__ ring) {
+  using T = In<IN>;
+  __shared__ uint32_t red[kQBlock / 64];
+  __shared__ int s_last;
+  uint32_t amag = 0;
+  auto take = [&](v4u v) __attribute__((always_inline)) {
+    if constexpr (T::kBits == 16) {
+      amag = max(amag, max(max(T::mag(v.x & 0xFFFFu), T::mag(v.x >> 16)), max(T::mag(v.y & 0xFFFFu), T::mag(v.y >> 16))));
+      amag = max(amag, max(max(T::mag(v.z & 0xFFFFu), T::mag(v.z >> 16)), max(T::mag(v.w & 0xFFFFu), T::mag(v.w >> 16))));
+    } else {
+      amag = max(amag, max(max(T::mag(v.x), T::mag(v.y)), max(T::mag(v.z), T::mag(v.w))));
+    }
+  };
+  const int64_t step = (int64_t)gridDim.x * kQBlock * kQUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
+    if (base + (kQUnroll - 1) * kQBlock < nchunk) {
+      v4u v[kQUnroll];
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kQBlock);
+#pragma unroll
+      for (int u = 0; u < kQUnroll; ++u) take(v[u]);
+    } else {
+      for (int u = 0; u < kQUnroll; ++u)
+        if (base + u * kQBlock < nchunk) take(x[base + u * kQBlock]);
+    }
+  }
+  if (tail > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int i = 0; i < tail; ++i) {
+      const uint32_t e = T::kBits == 16 ? reinterpret_cast<const uint16_t*>(x_tail)[i]
+                                        : reinterpret_cast<const uint32_t*>(x_tail)[i];
+      amag = max(amag, T::mag(e));
+    }
+  }
+  uint32_t a;
+  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
+  if (threadIdx.x == 0) {
+    const bool bad = ring->hist_len != 1 || ring->idx != 0;
+    if (bad || ring->fmt != FMT) {
+      ring->status |= (bad ? kStatusBadHeader : 0u) | (ring->fmt != FMT ? kStatusFmtMismatch : 0u);
+    } else {
+      float s = 1.0f;
+      if (a > 0u && a < 0x7F800000u) {
+        const float t = FmtTraits<FMT>::kMax / __uint_as_float(a);
+        if (__float_as_uint(t) < 0x7F800000u) s = t;
+      }
+      ring_hist(ring)[0] = __uint_as_float(a);
+      ring->scale = s;
+      ring->amax_last = __uint_as_float(a);
+    }
+    clear_top(ring);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Bias gradient: out[c] = sum_r g[r][c] in fp32, g bf16 / fp16 / fp32 or 8-bit
+// codes dequantized as dec(code) * s_inv.  A block takes 64 columns and a
+// slice of the rows; thread t sums columns 8*(t%8) .. +7 over rows t/8,
+// t/8 + 32, ... of its slice, the 32 row lanes are added in a fixed order in
+// LDS, and the slice's 64 sums go to the workspace.  The last block of a
+// column strip (a ticket per strip, as in the ring's completion tree) adds
+// the slices in order, so the result does not depend on timing.  Partial sums
+// travel as device-scope atomic stores and loads, so they are seen across
+// XCDs without writing back any cache.  The last block clears what it read
+// and its ticket: the whole workspace is zero again after every call, so one
+// workspace serves calls of any shape up to its size.
+
+constexpr int kGBf16 = 0, kGF16 = 1, kGF32 = 2, kGE4M3 = 3, kGE5M2 = 4;
+
+template <int GT>
+__device__ __forceinline__ void load8(const uint8_t* row, int col, float s_inv, float (&v)[8]) {
+  if constexpr (GT == kGBf16 || GT == kGF16) {
+    const v4u w = *reinterpret_cast<const v4u*>(row + col * 2);
+    const uint32_t e[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
+                           w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = GT == kGBf16 ? In<kInBf16>::f(e[i]) : In<kInF16>::f(e[i]);
+  } else if constexpr (GT == kGF32) {
+    const v4u w0 = *reinterpret_cast<const v4u*>(row + col * 4);
+    const v4u w1 = *reinterpret_cast<const v4u*>(row + col * 4 + 16);
+    const uint32_t e[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(e[i]);
+  } else {
+    const v2u w = *reinterpret_cast<const v2u*>(row + col);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = (int)((i < 4 ? w.x : w.y) >> (8 * (i & 3)));
+      const float d = GT == kGE4M3 ? __builtin_amdgcn_cvt_f32_fp8(c, 0) : __builtin_amdgcn_cvt_f32_bf8(c, 0);
+      v[i] = d * s_inv;
+    }
+  }
+}
+
+constexpr int kGradCols = 64;
+
+template <int GT>
+__global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __restrict__ g, int rows, int cols,
+                                                            int slices, int rows_per_slice,
+                                                            const float* __restrict__ g_scale_inv, int out_f32,
+                                                            void* __restrict__ out, float* __restrict__ partial,
+                                                            uint32_t* __restrict__ tickets) {
+  constexpr int kElem = GT == kGF32 ? 4 : (GT == kGBf16 || GT == kGF16) ? 2 : 1;
+  __shared__ float sums[32][kGradCols + 1];
+  __shared__ int s_last;
+  const int strip = blockIdx.x / slices, slice = blockIdx.x % slices;
+  const int c0 = strip * kGradCols;
+  const int cg = threadIdx.x & 7, rl = threadIdx.x >> 3;   // 8-column group, row lane
+  const int col = c0 + 8 * cg;
+  const float s_inv = (GT == kGE4M3 || GT == kGE5M2) ? g_scale_inv[0] : 1.0f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r_begin = slice * rows_per_slice;
+  const int r_end = min(rows, r_begin + rows_per_slice);
+  if (col < cols) {
+    for (int r = r_begin + rl; r < r_end; r += 32) {
+      float v[8];
+      load8<GT>(g + (int64_t)r * cols * kElem, col, s_inv, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sums[rl][8 * cg + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < kGradCols) {
+    float s = 0.f;
+    for (int j = 0; j < 32; ++j) s += sums[j][threadIdx.x];
+    if (c0 + threadIdx.x < cols)
+      __hip_atomic_store(partial + (int64_t)slice * cols + c0 + threadIdx.x, s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(tickets + strip, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(t);
+    s_last = t == (uint32_t)slices - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x < kGradCols && c0 + (int)threadIdx.x < cols) {
+    float s = 0.f;
+    for (int j = 0; j < slices; ++j) {
+      float* pp = partial + (int64_t)j * cols + c0 + threadIdx.x;
+      s += __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pp, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (out_f32) static_cast<float*>(out)[c0 + threadIdx.x] = s;
+    else static_cast<uint16_t*>(out)[c0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (__bf16)s);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(tickets + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void ring_init_kernel(RingHeader* ring, int hist_len, int fmt, float init_scale) {
@@ -249,6 +565,37 @@ __global__ __launch_bounds__(256) void ring_init_kernel(RingHeader* ring, int hi
   }
 }
 
+typedef void (*QuantFn)(const v4u*, uint8_t*, int64_t, const uint8_t*, uint8_t*, int, RingHeader*);
+typedef void (*AmaxFn)(const v4u*, int64_t, const uint8_t*, int, RingHeader*);
+typedef void (*Quant2dFn)(const uint8_t*, uint8_t*, uint8_t*, int, int, int, RingHeader*);
+
+template <int FMT>
+QuantFn quant_fn(int in) {
+  return in == kInBf16 ? quantize_kernel<FMT, kInBf16> : in == kInF16 ? quantize_kernel<FMT, kInF16>
+                                                                       : quantize_kernel<FMT, kInF32>;
+}
+template <int FMT>
+AmaxFn amax_fn(int in) {
+  return in == kInBf16 ? amax_kernel<FMT, kInBf16> : in == kInF16 ? amax_kernel<FMT, kInF16> : amax_kernel<FMT, kInF32>;
+}
+template <int FMT, bool DUAL>
+Quant2dFn quant2d_fn(int in) {
+  return in == kInBf16 ? quantize_2d_kernel<FMT, kInBf16, DUAL>
+         : in == kInF16 ? quantize_2d_kernel<FMT, kInF16, DUAL>
+                        : quantize_2d_kernel<FMT, kInF32, DUAL>;
+}
+
+int in_bytes(int in) { return in == kInF32 ? 4 : 2; }
+
+// Grid of a streaming launch over numel elements of the input type.
+int64_t stream_blocks(int64_t nchunk, int max_blocks) {
+  const int64_t per_block = (int64_t)kQBlock * kQUnroll;
+  int64_t blocks = (nchunk + per_block - 1) / per_block;
+  if (blocks < 1) blocks = 1;
+  if (max_blocks <= 0) max_blocks = kDefaultBlocks;
+  return blocks > max_blocks ? max_blocks : blocks;
+}
+
 }  // namespace
 
 int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStream_t stream) {
@@ -257,26 +604,85 @@ int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStr
   return check_launch("ring_init_kernel");
 }
 
-int launch_quantize(const void* x, int64_t numel, int fmt, void* ring, void* y, int max_blocks, hipStream_t stream) {
-  const int64_t nchunk = numel / 8;
-  const int tail = (int)(numel % 8);
-  const int64_t per_block = (int64_t)kQBlock * kQUnroll;
-  int64_t blocks = (nchunk + per_block - 1) / per_block;
-  if (blocks < 1) blocks = 1;
+int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y, int max_blocks,
+                    hipStream_t stream) {
+  const int eb = in_bytes(in_type);
+  const int per16 = 16 / eb;
+  const int64_t nchunk = numel / per16;
+  const int tail = (int)(numel % per16);
+  const int64_t blocks = stream_blocks(nchunk, max_blocks);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  uint8_t* yb = static_cast<uint8_t*>(y);
+  QuantFn fn = fmt == kE4M3 ? quant_fn<kE4M3>(in_type) : quant_fn<kE5M2>(in_type);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, reinterpret_cast<const v4u*>(xb), yb,
+                     nchunk, xb + nchunk * 16, yb + nchunk * per16, tail, static_cast<RingHeader*>(ring));
+  return check_launch("quantize_kernel");
+}
+
+int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, bool dual, void* ring, void* y,
+                       void* y_t, int max_blocks, hipStream_t stream) {
+  const int tiles_c = (cols + kTile - 1) / kTile;
+  const int64_t ntiles = (int64_t)((rows + kTile - 1) / kTile) * tiles_c;
+  int64_t blocks = ntiles < 1 ? 1 : ntiles;
   if (max_blocks <= 0) max_blocks = kDefaultBlocks;
   if (blocks > max_blocks) blocks = max_blocks;
-  const v4u* xv = static_cast<const v4u*>(x);
-  v2u* yv = static_cast<v2u*>(y);
-  const uint16_t* xt = static_cast<const uint16_t*>(x) + nchunk * 8;
-  uint8_t* yt = static_cast<uint8_t*>(y) + nchunk * 8;
-  RingHeader* r = static_cast<RingHeader*>(ring);
-  if (fmt == kE4M3)
-    hipLaunchKernelGGL(quantize_kernel<kE4M3>, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, xv, yv, nchunk, xt,
-                       yt, tail, r);
-  else
-    hipLaunchKernelGGL(quantize_kernel<kE5M2>, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, xv, yv, nchunk, xt,
-                       yt, tail, r);
-  return check_launch("quantize_kernel");
+  Quant2dFn fn = fmt == kE4M3 ? (dual ? quant2d_fn<kE4M3, true>(in_type) : quant2d_fn<kE4M3, false>(in_type))
+                              : (dual ? quant2d_fn<kE5M2, true>(in_type) : quant2d_fn<kE5M2, false>(in_type));
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, static_cast<const uint8_t*>(x),
+                     static_cast<uint8_t*>(y), static_cast<uint8_t*>(y_t), rows, cols, tiles_c,
+                     static_cast<RingHeader*>(ring));
+  return check_launch("quantize_2d_kernel");
+}
+
+int launch_amax(const void* x, int64_t numel, int in_type, int fmt, void* ring, hipStream_t stream) {
+  const int eb = in_bytes(in_type);
+  const int per16 = 16 / eb;
+  const int64_t nchunk = numel / per16;
+  const int tail = (int)(numel % per16);
+  const int64_t blocks = stream_blocks(nchunk, 0);
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  AmaxFn fn = fmt == kE4M3 ? amax_fn<kE4M3>(in_type) : amax_fn<kE5M2>(in_type);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, reinterpret_cast<const v4u*>(xb), nchunk,
+                     xb + nchunk * 16, tail, static_cast<RingHeader*>(ring));
+  return check_launch("amax_kernel");
+}
+
+// Row slices per 64-column strip: enough blocks to cover the CUs four times
+// over, each slice at least 32 rows.  A function of the shape only, so the
+// summation order (and the result) is fixed for a shape.
+int bias_grad_slices(int64_t rows, int64_t cols) {
+  const int64_t strips = (cols + kGradCols - 1) / kGradCols;
+  int64_t s = (1024 + strips - 1) / strips;
+  const int64_t max_s = (rows + 31) / 32;
+  if (s > max_s) s = max_s;
+  if (s > 256) s = 256;
+  return (int)(s < 1 ? 1 : s);
+}
+
+// Workspace: one ticket per 64-column strip, then the slices' partial sums.
+size_t bias_grad_tickets_bytes(int64_t cols) {
+  const int64_t strips = (cols + kGradCols - 1) / kGradCols;
+  return ((size_t)strips * 4 + 255) & ~(size_t)255;
+}
+
+size_t bias_grad_workspace(int64_t rows, int64_t cols) {
+  return bias_grad_tickets_bytes(cols) + (size_t)bias_grad_slices(rows, cols) * (size_t)cols * 4;
+}
+
+int launch_bias_grad(const void* g, int rows, int cols, int g_type, const float* g_scale_inv, int out_f32, void* out,
+                     void* workspace, hipStream_t stream) {
+  const int slices = bias_grad_slices(rows, cols);
+  const int rps = (rows + slices - 1) / slices;
+  const int strips = (cols + kGradCols - 1) / kGradCols;
+  uint32_t* tickets = static_cast<uint32_t*>(workspace);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + bias_grad_tickets_bytes(cols));
+  typedef void (*Fn)(const uint8_t*, int, int, int, int, const float*, int, void*, float*, uint32_t*);
+  const Fn fns[] = {bias_grad_kernel<kGBf16>, bias_grad_kernel<kGF16>, bias_grad_kernel<kGF32>,
+                    bias_grad_kernel<kGE4M3>, bias_grad_kernel<kGE5M2>};
+  hipLaunchKernelGGL(fns[g_type], dim3((unsigned)(strips * slices)), dim3(kQBlock), 0, stream,
+                     static_cast<const uint8_t*>(g), rows, cols, slices, rps, g_scale_inv, out_f32, out, partial,
+                     tickets);
+  return check_launch("bias_grad_kernel");
 }
 
 }  // namespace fp8ds

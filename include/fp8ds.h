@@ -36,8 +36,35 @@ typedef enum { FP8DS_E4M3 = 0, FP8DS_E5M2 = 1 } fp8ds_fmt;
 typedef enum { FP8DS_NT = 0, FP8DS_NN = 1, FP8DS_TN = 2 } fp8ds_layout;
 
 /* Bias storage (bias-fusion entry, fp8.py history @f4c44ebf): none, bf16[N]
- * or fp32[N]; added in fp32 before the single bf16 rounding. */
-typedef enum { FP8DS_BIAS_NONE = 0, FP8DS_BIAS_BF16 = 1, FP8DS_BIAS_F32 = 2 } fp8ds_bias_kind;
+ * or fp32[N], or 8-bit codes[N] dequantized as dec(code) * bias_scale_inv
+ * (history of test_fp8_mma.py, bias_scale entry); added in fp32 before the
+ * single bf16 rounding. */
+typedef enum {
+  FP8DS_BIAS_NONE = 0,
+  FP8DS_BIAS_BF16 = 1,
+  FP8DS_BIAS_F32 = 2,
+  FP8DS_BIAS_E4M3 = 3,
+  FP8DS_BIAS_E5M2 = 4
+} fp8ds_bias_kind;
+
+/* Element type a quantize reads (fp8.py history @f4c44ebf, entry templating
+ * the quantize on its input type). */
+typedef enum { FP8DS_IN_BF16 = 0, FP8DS_IN_F16 = 1, FP8DS_IN_F32 = 2 } fp8ds_in_type;
+
+/* Orientation of a 2-D quantize (history of `tests`, entry splitting the
+ * quantize into quantize / quantize_dual with a layout enum). */
+typedef enum { FP8DS_ROWWISE = 0, FP8DS_TRANSPOSED = 1, FP8DS_DUAL = 2 } fp8ds_quant_layout;
+
+/* Element type of a gradient summed by fp8_bias_grad: raw bf16 / fp16 / fp32,
+ * or 8-bit codes dequantized with a scale (fp8.py history @f4c44ebf,
+ * pre-quantized g entry). */
+typedef enum {
+  FP8DS_G_BF16 = 0,
+  FP8DS_G_F16 = 1,
+  FP8DS_G_F32 = 2,
+  FP8DS_G_E4M3 = 3,
+  FP8DS_G_E5M2 = 4
+} fp8ds_grad_type;
 
 enum {
   FP8DS_OK = 0,
@@ -117,6 +144,58 @@ int fp8_quantize(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y
 int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* ring, void* y_fp8, int max_blocks,
                            void* stream);
 
+/* fp8_quantize of an input of any fp8ds_in_type (fp8.py history @f4c44ebf,
+ * input-type entry): the element is widened to fp32 exactly, then as above;
+ * amax is max |fl32(x)|.  x: device, numel elements of in_type, 16-byte
+ * aligned.  Same errors as fp8_quantize; in_type outside the enum is
+ * FP8DS_EINVAL. */
+int fp8_quantize_ex(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream);
+
+/* Quantize of a rows x cols row-major tensor in one or two orientations
+ * (history of `tests`: quantize / quantize_dual, orientations byte-equal to
+ * the plain quantize):
+ *   ROWWISE:    y[r][c]   = code of x[r][c]          (y: rows x cols)
+ *   TRANSPOSED: y_t[c][r] = code of x[r][c]          (y_t: cols x rows)
+ *   DUAL:       both, from one read of x.
+ * The codes and the ring update are exactly those of fp8_quantize_ex on the
+ * same elements (one amax fold per call).  x: device, 16-byte aligned; y and
+ * y_t: device, 16-byte aligned, unused ones may be NULL; neither may overlap
+ * x.  TRANSPOSED and DUAL need rows and cols to be multiples of 16
+ * (FP8DS_EALIGN otherwise) and rows, cols < 2^31.  rows == 0 or cols == 0
+ * launches nothing. */
+int fp8_quantize_2d(const void* x, int64_t rows, int64_t cols, int in_type, int fmt, int layout, void* ring, void* y,
+                    void* y_t, void* stream);
+
+/* Dynamic-scaling quantize: the tensor's own amax sets its scale
+ * (fp8.py history @4dc5e923, dynamic-path entry; history of `tests`, recipe
+ * with a dynamic flag).  Two launches on `stream`: a read of x that leaves in
+ * ring hist[0] = a = max |fl32(x)| and scale = FMAX / a (1 if a is zero,
+ * infinite or NaN or the quotient overflows), then fp8_quantize_ex with that
+ * scale, after which scale_inv_used = 1 / scale and amax_last = a.
+ * ring: an initialised ring with hist_len 1 and format fmt (status bit 2 is
+ * set otherwise, and the ring and y are then unspecified).  Other arguments
+ * and errors as fp8_quantize_ex. */
+int fp8_quantize_dynamic(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream);
+
+/* Bias gradient (fp8.py history @f4c44ebf: the column sum of the output
+ * gradient, run only when the bias needs a gradient; a pre-quantized g is
+ * dequantized before the sum; gradients are bf16):
+ *   out[c] = sum_r g[r][c]   accumulated in fp32, rounded once to bf16
+ *                            (out_f32 == 0) or stored as fp32 (out_f32 != 0)
+ * g: device, rows x cols row-major of g_type; 8-bit codes are dequantized as
+ * fl32(dec(code) * g_scale_inv[0]) (g_scale_inv: device fp32, unused for the
+ * other types).  cols must be a multiple of 8 and g 16-byte aligned.
+ * The summation order depends only on (rows, cols): results are the same
+ * bits run to run.  workspace: device, at least
+ * fp8_bias_grad_workspace_bytes(rows, cols) bytes, 16-byte aligned,
+ * zero-filled before its first use; every call leaves it all zero again, so
+ * one workspace serves calls of any shape whose size it covers (calls sharing
+ * a workspace must be ordered on one stream).  cols == 0 launches nothing;
+ * rows == 0 writes zeros. */
+size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
+int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv, int out_f32,
+                  void* out, void* workspace, void* stream);
+
 /* Scaled FP8 GEMM arguments.  Zero-initialise and set what you use: a
  * zeroed field means "absent" (gemm.cuh history @5e76fbd1, null-default
  * params entry). */
@@ -133,7 +212,8 @@ typedef struct fp8_mm_args {
   int64_t stride_a, stride_b, stride_c; /* batch strides in elements; 0 broadcasts a/b */
   const float* a_scale_inv; /* device fp32 scalar, e.g. fp8_ring_scale_inv(ring_a)   */
   const float* b_scale_inv; /* device fp32 scalar                                    */
-  const void* bias;         /* device bf16[N] or fp32[N], broadcast over rows, batch */
+  const void* bias;         /* device bf16[N], fp32[N] or codes[N], broadcast over rows, batch */
+  const float* bias_scale_inv; /* device fp32 scalar for an 8-bit bias, else unused  */
 } fp8_mm_args;
 
 /* Scaled FP8 GEMM (gemm.cuh history @5e76fbd1; fp8.py history @f4c44ebf,

@@ -91,3 +91,36 @@ def test_validation_errors_launch_nothing(L):
     assert L.fp8_mm(ctypes.byref(args), None) == -1
     args.m, args.k, args.lda, args.ldb = 1 << 20, 1 << 12, 1 << 12, 1 << 12       # 4 GiB operand
     assert L.fp8_mm(ctypes.byref(args), None) == -3
+
+
+def test_widened_entry_points_validate_before_launch(L):
+    v = ctypes.c_void_p
+    ring = v(4096)
+    # bad input type / layout / misaligned transposed shapes
+    assert L.fp8_quantize_ex(v(64), 16, 7, 0, ring, v(128), None) == -1
+    assert b"in_type" in L.fp8_last_error()
+    assert L.fp8_quantize_ex(v(64), 0, 2, 0, ring, v(128), None) == 0             # empty: no-op
+    assert L.fp8_quantize_2d(v(64), 16, 16, 0, 0, 9, ring, v(128), v(256), None) == -1
+    x, yt = v(1 << 20), v(1 << 24)
+    assert L.fp8_quantize_2d(x, 24, 16, 0, 0, 1, ring, None, yt, None) == -2
+    assert L.fp8_quantize_2d(x, 16, 16, 0, 0, 2, ring, None, yt, None) == -1          # DUAL without y
+    assert L.fp8_quantize_2d(v(64), 0, 16, 0, 0, 2, ring, None, None, None) == 0       # empty: no-op
+    assert L.fp8_quantize_dynamic(v(64), 16, 0, 0, None, v(128), None) == -3
+    # bias gradient
+    assert L.fp8_bias_grad_workspace_bytes(2048, 4096) > 0
+    assert L.fp8_bias_grad_workspace_bytes(-1, 8) == 0
+    assert L.fp8_bias_grad(v(64), 16, 12, 0, None, 0, v(128), v(256), None) == -2      # cols % 8
+    assert L.fp8_bias_grad(v(64), 16, 16, 3, None, 0, v(128), v(256), None) == -1      # codes need a scale
+    assert L.fp8_bias_grad(v(64), 16, 16, 9, None, 0, v(128), v(256), None) == -1
+    assert L.fp8_bias_grad(v(64), 16, 0, 0, None, 0, None, None, None) == 0            # no columns: no-op
+    # GEMM 8-bit bias needs its scale
+    args = ds._MmArgs()
+    args.m, args.n, args.k = 16, 16, 16
+    args.a, args.b, args.c = 4096, 8192, 16384
+    args.a_scale_inv, args.b_scale_inv = 32768, 32768
+    args.lda, args.ldb, args.ldc = 16, 16, 16
+    args.bias, args.bias_kind = 40960, 3
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
+    assert b"bias_scale_inv" in L.fp8_last_error()
+    args.bias_kind = 5
+    assert L.fp8_mm(ctypes.byref(args), None) == -1
