@@ -41,13 +41,14 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-rows", type=int, default=256, help="output rows of the oracle sample")
+    ap.add_argument("--no-widened", action="store_true", help="skip the widened-path kernel timings")
     return ap.parse_args()
 
 
 def traffic_from_profile(kernel_src, sha_key, bytes_key):
     """HBM bytes per launch recorded in profiles/ by the two PMC runs, or
     None when the kernel source changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", "gemm_nt_8192_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_8192_bench_kernels.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -82,6 +83,72 @@ def cpu_baseline(a_bits, b_bits, size, rows):
             "sample": (f"first {rows} of {size} output rows: quantize B ({size}x{size}) and {rows} rows of A, "
                        f"fp64 GEMM of the slice; {dt:.1f} s; numpy elementwise steps on 1 thread, "
                        f"the fp64 matmul on {blas_threads} BLAS threads")}
+
+
+def time_launches(fn, stream, reps=10, warmup=3):
+    """Average duration of fn() in microseconds: HIP events on the launch
+    stream around `reps` back-to-back calls, after `warmup` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def measure_widened(ds, n, stream):
+    """Rooflines of the path's other kernels on n x n operands: the transposed
+    and dual quantize, the dynamic recipe (amax pass + quantize), fp32 and
+    fp16 inputs, the bias gradient of an n x n gradient, and the dX / dW GEMM
+    layouts in the backward formats (E5M2 x E4M3)."""
+    import torch
+    from synth import bf16_normal, seed_for
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(bf16_normal((n, n), seed_for(3, 0, "X")).view("int16")).view(torch.bfloat16).to(dev)
+    y = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    yt = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    ring = ds.ScaleRing(16, ds.E4M3)
+    ring1 = ds.ScaleRing(1, ds.E4M3)
+    out = {}
+
+    def hbm(name, us, nbytes, workload):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "avg_launch_us": round(us, 2),
+                     "bytes_per_launch": nbytes, "workload": workload}
+
+    us = time_launches(lambda: ds.fp8_quantize_2d(x, ds.E4M3, ring, ds.TRANSPOSED, out_t=yt), stream)
+    hbm("quantize_2d_transposed", us, 3.0 * n * n, f"{n}x{n} bf16 -> E4M3 codes of x^T, history 16")
+    us = time_launches(lambda: ds.fp8_quantize_2d(x, ds.E4M3, ring, ds.DUAL, out=y, out_t=yt), stream)
+    hbm("quantize_2d_dual", us, 4.0 * n * n, f"{n}x{n} bf16 -> E4M3 codes of x and x^T, history 16")
+    us = time_launches(lambda: ds.fp8_quantize_dynamic(x, ds.E4M3, ring1, out=y), stream)
+    hbm("quantize_dynamic", us, 5.0 * n * n, f"{n}x{n} bf16, amax pass + quantize pass (two launches)")
+    x32 = x.float()
+    us = time_launches(lambda: ds.fp8_quantize(x32, ds.E4M3, ring, out=y), stream)
+    hbm("quantize_fp32_input", us, 5.0 * n * n, f"{n}x{n} fp32 -> E4M3, history 16")
+    del x32
+    x16 = x.half()
+    us = time_launches(lambda: ds.fp8_quantize(x16, ds.E4M3, ring, out=y), stream)
+    hbm("quantize_fp16_input", us, 3.0 * n * n, f"{n}x{n} fp16 -> E4M3, history 16")
+    del x16
+    ws = ds.BiasGradWorkspace(n, n)
+    gb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    us = time_launches(lambda: ds.fp8_bias_grad(x, out=gb, workspace=ws), stream)
+    hbm("bias_grad", us, 2.0 * n * n + 2.0 * n, f"column sums of a {n}x{n} bf16 gradient, bf16 out")
+    a8 = torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev)
+    b8 = torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for name, layout in (("gemm_nn_dx", ds.NN), ("gemm_tn_dw", ds.TN)):
+        us = time_launches(lambda: ds.fp8_mm(a8, b8, ds.E5M2, ds.E4M3, layout, n, n, n, ring, ring, out=c), stream)
+        tf = 2.0 * n ** 3 / (us * 1e-6) / 1e12
+        out[name] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_FP8_TFLOPS, 4), "avg_launch_us": round(us, 2),
+                     "workload": f"{n}^3 {'NN' if layout == ds.NN else 'TN'} E5M2 x E4M3, bf16 out"}
+    return out
 
 
 def main():
@@ -187,6 +254,21 @@ def main():
                               "bytes_per_launch": q_bytes,
                               "avg_launch_us": round(q_avg * 1e3, 2)},
     }
+    if not args.no_widened:
+        del A, B, A8, B8, C, cal_src, cal_dst
+        torch.cuda.empty_cache()
+        out["widened"] = measure_widened(ds, n, stream)
+        qsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip")
+        gsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip")
+        for name, entry in out["widened"].items():
+            src, sha_key = (gsrc, "kernel_source_sha256") if name.startswith("gemm") else (qsrc, "quantize_source_sha256")
+            key = {"gemm_nn_dx": "gemm_nn", "gemm_tn_dw": "gemm_tn"}.get(name, name) + "_hbm_bytes_per_launch"
+            if name == "quantize_dynamic":
+                a = traffic_from_profile(qsrc, sha_key, "amax_hbm_bytes_per_launch")
+                q = traffic_from_profile(qsrc, sha_key, "quantize_hbm_bytes_per_launch")
+                entry["traffic"] = None if a is None or q is None else a + q
+            else:
+                entry["traffic"] = traffic_from_profile(src, sha_key, key)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(a_bits, b_bits, n, min(args.cpu_rows, n))
     print(json.dumps(out), flush=True)

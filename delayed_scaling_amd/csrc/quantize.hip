@@ -302,13 +302,18 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
 
 // ---------------------------------------------------------------------------
 // Transposed / dual quantize of an R x C row-major tensor, R and C multiples
-// of 16.  A block takes a 64 x 64 tile: each thread quantizes 16 consecutive
-// elements of one row (and, for the dual form, stores those 16 codes), then
-// writes them to an LDS tile [64 rows][64 codes] whose 16-byte chunks are
-// XOR-swizzled per row; transpose reads (ds_read_b64_tr_b8) hand each lane 16
-// consecutive rows of one column, stored as 16 bytes of the transposed output.
+// of 16.  A block takes a 128-row x 64-column tile:
+//  1. threads quantize 16-byte pieces of the tile's rows, consecutive threads
+//     on consecutive pieces (and, for the dual form, store those codes), and
+//     write the codes to an LDS tile [128 rows][64 codes] whose 16-byte chunks
+//     are XOR-swizzled per row;
+//  2. transpose reads (ds_read_b64_tr_b8) hand each lane 32 consecutive rows
+//     of one column, which it writes to a second LDS tile [64 columns][128
+//     rows] (rows padded to 144 bytes against bank conflicts);
+//  3. eight lanes per column then store 16 bytes each: every store
+//     instruction writes whole 128-byte lines of the transposed output.
 
-constexpr int kTile = 64;
+constexpr int kTileR = 128, kTileC = 64, kTStride = kTileR + 16;
 
 __device__ __forceinline__ int tile_swz(int r) { return ((r >> 2) & 1) << 1; }
 
@@ -318,64 +323,85 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
                                                               int tiles_c, RingHeader* __restrict__ ring) {
   using T = In<IN>;
   constexpr int kElemBytes = T::kBits / 8;
-  __shared__ __attribute__((aligned(16))) char codes_lds[kTile * kTile];
+  __shared__ __attribute__((aligned(16))) char codes_lds[kTileR * kTileC];
+  __shared__ __attribute__((aligned(16))) char trans_lds[kTileC * kTStride];
   __shared__ uint32_t red[kQBlock / 64];
   __shared__ int s_last;
   const float scale = ring->scale;
   uint32_t amag = 0;
   lds_char_t* tile = (lds_char_t*)codes_lds;
+  lds_char_t* ttile = (lds_char_t*)trans_lds;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tr = threadIdx.x >> 2, tch = threadIdx.x & 3;    // row in tile, 16-column chunk
-  const int ntiles = ((rows + kTile - 1) / kTile) * tiles_c;
+  const int ntiles = ((rows + kTileR - 1) / kTileR) * tiles_c;
+  // Loads: 16 bytes each, kPer elements; kLoads per tile row, consecutive
+  // threads on consecutive pieces of a row, so each load instruction reads
+  // whole 128-byte lines.
+  constexpr int kPer = 16 / kElemBytes, kLoads = kTileC / kPer, kIters = kTileR * kLoads / kQBlock;
+  constexpr int kWords = kPer / 4;                            // code words per load
   for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int r0 = (t / tiles_c) * kTile, c0 = (t % tiles_c) * kTile;
-    const int r = r0 + tr, c = c0 + tch * 16;
-    const bool in = r < rows && c < cols;                     // cols % 16 == 0: whole chunk in or out
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (in) {
-      const v4u* src = reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes);
-      uint32_t o[2];
-      if constexpr (T::kBits == 16) {
-        quant16<FMT, IN>(__builtin_nontemporal_load(src), scale, o, amag);
-        w[0] = o[0]; w[1] = o[1];
-        quant16<FMT, IN>(__builtin_nontemporal_load(src + 1), scale, o, amag);
-        w[2] = o[0]; w[3] = o[1];
-      } else {
+    const int r0 = (t / tiles_c) * kTileR, c0 = (t % tiles_c) * kTileC;
+    uint32_t w[kIters][2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          quant16<FMT, IN>(__builtin_nontemporal_load(src + q), scale, o, amag);
-          w[q] = o[0];
+    for (int j = 0; j < kIters; ++j) {
+      const int item = threadIdx.x + j * kQBlock;
+      const int tr = item / kLoads, piece = item % kLoads;
+      const int r = r0 + tr, c = c0 + piece * kPer;
+      w[j][0] = w[j][1] = 0u;
+      if (r < rows && c < cols) {                            // cols % 16 == 0: whole load in or out
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes));
+        quant16<FMT, IN>(v, scale, w[j], amag);
+        if constexpr (DUAL) {
+          if constexpr (kWords == 2)
+            __builtin_nontemporal_store(v2u{w[j][0], w[j][1]}, reinterpret_cast<v2u*>(y + (int64_t)r * cols + c));
+          else
+            __builtin_nontemporal_store(w[j][0], reinterpret_cast<uint32_t*>(y + (int64_t)r * cols + c));
         }
       }
-      if constexpr (DUAL)
-        __builtin_nontemporal_store(v4u{w[0], w[1], w[2], w[3]}, reinterpret_cast<v4u*>(y + (int64_t)r * cols + c));
     }
-    __syncthreads();   // the previous tile's transpose reads are done
-    *(lds_v4i_t*)(tile + tr * kTile + ((tch ^ tile_swz(tr)) << 4)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    __syncthreads();
-    // Transposed store: lane l of wave w takes column c0 + 32*(w&1) + l%32
-    // and tile rows 32*(l/32) + 16*(w>>1) + [0, 16): two transpose reads of
-    // 8 rows each.
-    // Within each 16-lane group, the even lanes address rows k..k+7 of the
-    // group's first 8 columns and the odd lanes the next 8; a read hands each
-    // lane 8 consecutive rows of one column.
-    const int col = 32 * (wave & 1) + (lane & 31);
-    const int rbase = 32 * (lane >> 5) + 16 * (wave >> 1);
-    const int q = lane & 15;
-    const int chunk = 2 * (wave & 1) + ((lane >> 4) & 1);
-    v2i part[2];
+    __syncthreads();   // the previous tile's reads of both LDS tiles are done
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kr = rbase + 8 * h + (q >> 1);
-      const int addr = kr * kTile + ((chunk ^ tile_swz(kr)) << 4) + 8 * (q & 1);
-      part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(tile + addr));
+    for (int j = 0; j < kIters; ++j) {
+      const int item = threadIdx.x + j * kQBlock;
+      const int tr = item / kLoads, piece = item % kLoads;
+      const int byte = piece * kPer;                          // code byte in the row
+      lds_char_t* p = tile + tr * kTileC + (((byte >> 4) ^ tile_swz(tr)) << 4) + (byte & 15);
+      if constexpr (kWords == 2) *(lds_v2i_t*)p = v2i{(int)w[j][0], (int)w[j][1]};
+      else *(__attribute__((address_space(3))) int*)p = (int)w[j][0];
     }
-    const int oc = c0 + col, orow = r0 + rbase;
-    if (oc < cols && orow < rows)
-      __builtin_nontemporal_store(v4u{(uint32_t)part[0][0], (uint32_t)part[0][1], (uint32_t)part[1][0],
-                                      (uint32_t)part[1][1]},
-                                  reinterpret_cast<v4u*>(y_t + (int64_t)oc * rows + orow));
+    __syncthreads();
+    {
+      // Lane l of wave w takes column 32*(w&1) + l%32 and tile rows
+      // 64*(w>>1) + 32*(l/32) + [0, 32).  Within each 16-lane group, the even
+      // lanes address rows k..k+7 of the group's first 8 columns and the odd
+      // lanes the next 8; each read hands a lane 8 consecutive rows of its
+      // column.
+      const int col = 32 * (wave & 1) + (lane & 31);
+      const int rbase = 64 * (wave >> 1) + 32 * (lane >> 5);
+      const int q = lane & 15;
+      const int chunk = 2 * (wave & 1) + ((lane >> 4) & 1);
+      v2i part[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int kr = rbase + 8 * h + (q >> 1);
+        const int addr = kr * kTileC + ((chunk ^ tile_swz(kr)) << 4) + 8 * (q & 1);
+        part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(tile + addr));
+      }
+      lds_char_t* dst = ttile + col * kTStride + rbase;
+      *(lds_v4i_t*)dst = v4i{part[0][0], part[0][1], part[1][0], part[1][1]};
+      *(lds_v4i_t*)(dst + 16) = v4i{part[2][0], part[2][1], part[3][0], part[3][1]};
+    }
+    __syncthreads();
+    // Eight lanes per column, 16 bytes each: column t/8 + 32*j, rows
+    // 16*(t%8) + [0, 16) of the tile.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = (threadIdx.x >> 3) + 32 * j, piece = threadIdx.x & 7;
+      const int oc = c0 + col, orow = r0 + 16 * piece;
+      const v4i v = *(const lds_v4i_t*)(ttile + col * kTStride + 16 * piece);
+      if (oc < cols && orow < rows)
+        *reinterpret_cast<v4i*>(y_t + (int64_t)oc * rows + orow) = v;
+    }
   }
 
   uint32_t a;
@@ -621,8 +647,8 @@ int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ri
 
 int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, bool dual, void* ring, void* y,
                        void* y_t, int max_blocks, hipStream_t stream) {
-  const int tiles_c = (cols + kTile - 1) / kTile;
-  const int64_t ntiles = (int64_t)((rows + kTile - 1) / kTile) * tiles_c;
+  const int tiles_c = (cols + kTileC - 1) / kTileC;
+  const int64_t ntiles = (int64_t)((rows + kTileR - 1) / kTileR) * tiles_c;
   int64_t blocks = ntiles < 1 ? 1 : ntiles;
   if (max_blocks <= 0) max_blocks = kDefaultBlocks;
   if (blocks > max_blocks) blocks = max_blocks;
