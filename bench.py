@@ -151,6 +151,60 @@ def measure_widened(ds, n, stream):
     return out
 
 
+def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
+    """Forward + backward of the linear layers of a 12-layer, dim-1024 model on
+    2048 tokens (per layer QKV 1024->3072, O 1024->1024, MLP up 1024->4096 and
+    down 4096->1024, no bias): the library's FP8 layer against torch's bf16
+    linear, each linear with its own synthetic input and output gradient."""
+    import torch
+    from delayed_scaling_amd.linear import Fp8Linear
+    shapes = [(dim, 3 * dim), (dim, dim), (dim, 4 * dim), (4 * dim, dim)] * layers
+    gen = torch.Generator("cuda").manual_seed(4000)
+    xs = [torch.randn(tokens, i, device="cuda", generator=gen).to(torch.bfloat16).requires_grad_() for i, _ in shapes]
+    gs = [(torch.randn(tokens, o, device="cuda", generator=gen) * 1e-3).to(torch.bfloat16) for _, o in shapes]
+    fp8 = [Fp8Linear(i, o, bias=False) for i, o in shapes]
+    bf16 = [torch.nn.Linear(i, o, bias=False, device="cuda", dtype=torch.bfloat16) for i, o in shapes]
+
+    def run(mods):
+        for m, x, g in zip(mods, xs, gs):
+            m(x).backward(g)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    res = {}
+    for name, mods in (("fp8", fp8), ("bf16", bf16)):
+        for _ in range(2):
+            run(mods)
+        res[name + "_eager"] = timed(lambda: run(mods))
+        # The same step captured once in a HIP graph and replayed: no host work per call.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run(mods)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run(mods)
+        graph.replay()
+        res[name] = timed(graph.replay)
+    flops = 6.0 * tokens * sum(i * o for i, o in shapes)
+    return {"workload": f"{layers} layers x 4 linears (dim {dim}, {tokens} tokens), forward + backward, no bias, "
+                        "each step captured in a HIP graph",
+            "fp8_ms_per_step": round(res["fp8"], 3), "bf16_ms_per_step": round(res["bf16"], 3),
+            "speedup_vs_bf16": round(res["bf16"] / res["fp8"], 3),
+            "fp8_tflops": round(flops / (res["fp8"] * 1e-3) / 1e12, 1),
+            "bf16_tflops": round(flops / (res["bf16"] * 1e-3) / 1e12, 1),
+            "eager_fp8_ms_per_step": round(res["fp8_eager"], 3), "eager_bf16_ms_per_step": round(res["bf16_eager"], 3)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -258,9 +312,12 @@ def main():
         del A, B, A8, B8, C, cal_src, cal_dst
         torch.cuda.empty_cache()
         out["widened"] = measure_widened(ds, n, stream)
+        out["widened"]["linear_step_12_layers"] = measure_linear_step(stream)
         qsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip")
         gsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip")
         for name, entry in out["widened"].items():
+            if "bound" not in entry:
+                continue
             src, sha_key = (gsrc, "kernel_source_sha256") if name.startswith("gemm") else (qsrc, "quantize_source_sha256")
             key = {"gemm_nn_dx": "gemm_nn", "gemm_tn_dw": "gemm_tn"}.get(name, name) + "_hbm_bytes_per_launch"
             if name == "quantize_dynamic":
