@@ -85,32 +85,37 @@ def cpu_baseline(a_bits, b_bits, size, rows):
                        f"the fp64 matmul on {blas_threads} BLAS threads")}
 
 
-def time_launches(fn, stream, reps=10, warmup=3):
-    """Average duration of fn() in microseconds: HIP events on the launch
-    stream around `reps` back-to-back calls, after `warmup` calls."""
+def time_launches(fn, stream, reps=12, warmup=3):
+    """Average duration of fn(i) in microseconds: HIP events on the launch
+    stream around `reps` back-to-back calls, after `warmup` calls.  i counts
+    the calls, so fn can rotate over input copies."""
     import torch
-    for _ in range(warmup):
-        fn()
+    for i in range(warmup):
+        fn(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(reps):
-        fn()
+    for i in range(reps):
+        fn(warmup + i)
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def measure_widened(ds, n, stream):
-    """Rooflines of the path's other kernels on n x n operands: the transposed
-    and dual quantize, the dynamic recipe (amax pass + quantize), fp32 and
-    fp16 inputs, the bias gradient of an n x n gradient, and the dX / dW GEMM
-    layouts in the backward formats (E5M2 x E4M3)."""
+def measure_widened(ds, n, stream, rot=3):
+    """Rooflines of the path's other kernels on n x n operands: the single-
+    tensor quantize, the transposed and dual quantize, the dynamic recipe
+    (amax pass + quantize), fp32 and fp16 inputs, the bias gradient of an
+    n x n gradient, and the dX / dW GEMM layouts in the backward formats
+    (E5M2 x E4M3).  Every launch takes the next of `rot` input and output
+    copies, so the 256 MB Infinity Cache cannot carry one launch's data into
+    the next."""
     import torch
     from synth import bf16_normal, seed_for
     dev = torch.device("cuda:0")
-    x = torch.from_numpy(bf16_normal((n, n), seed_for(3, 0, "X")).view("int16")).view(torch.bfloat16).to(dev)
-    y = torch.empty((n, n), dtype=torch.uint8, device=dev)
-    yt = torch.empty((n, n), dtype=torch.uint8, device=dev)
+    x0 = torch.from_numpy(bf16_normal((n, n), seed_for(3, 0, "X")).view("int16")).view(torch.bfloat16).to(dev)
+    X = [x0] + [x0.clone() for _ in range(rot - 1)]
+    Y = [torch.empty((n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    YT = [torch.empty((n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
     ring = ds.ScaleRing(16, ds.E4M3)
     ring1 = ds.ScaleRing(1, ds.E4M3)
     out = {}
@@ -121,29 +126,35 @@ def measure_widened(ds, n, stream):
                      "frac": round(gbps / PEAK_HBM_GBPS, 4), "avg_launch_us": round(us, 2),
                      "bytes_per_launch": nbytes, "workload": workload}
 
-    us = time_launches(lambda: ds.fp8_quantize_2d(x, ds.E4M3, ring, ds.TRANSPOSED, out_t=yt), stream)
+    us = time_launches(lambda i: ds.fp8_quantize(X[i % rot], ds.E4M3, ring, out=Y[i % rot]), stream)
+    hbm("quantize_single", us, 3.0 * n * n, f"{n}x{n} bf16 -> E4M3, history 16, one tensor per launch")
+    us = time_launches(lambda i: ds.fp8_quantize_2d(X[i % rot], ds.E4M3, ring, ds.TRANSPOSED, out_t=YT[i % rot]),
+                       stream)
     hbm("quantize_2d_transposed", us, 3.0 * n * n, f"{n}x{n} bf16 -> E4M3 codes of x^T, history 16")
-    us = time_launches(lambda: ds.fp8_quantize_2d(x, ds.E4M3, ring, ds.DUAL, out=y, out_t=yt), stream)
+    us = time_launches(lambda i: ds.fp8_quantize_2d(X[i % rot], ds.E4M3, ring, ds.DUAL, out=Y[i % rot],
+                                                    out_t=YT[i % rot]), stream)
     hbm("quantize_2d_dual", us, 4.0 * n * n, f"{n}x{n} bf16 -> E4M3 codes of x and x^T, history 16")
-    us = time_launches(lambda: ds.fp8_quantize_dynamic(x, ds.E4M3, ring1, out=y), stream)
+    us = time_launches(lambda i: ds.fp8_quantize_dynamic(X[i % rot], ds.E4M3, ring1, out=Y[i % rot]), stream)
     hbm("quantize_dynamic", us, 5.0 * n * n, f"{n}x{n} bf16, amax pass + quantize pass (two launches)")
-    x32 = x.float()
-    us = time_launches(lambda: ds.fp8_quantize(x32, ds.E4M3, ring, out=y), stream)
-    hbm("quantize_fp32_input", us, 5.0 * n * n, f"{n}x{n} fp32 -> E4M3, history 16")
-    del x32
-    x16 = x.half()
-    us = time_launches(lambda: ds.fp8_quantize(x16, ds.E4M3, ring, out=y), stream)
+    x16 = [x.half() for x in X]
+    us = time_launches(lambda i: ds.fp8_quantize(x16[i % rot], ds.E4M3, ring, out=Y[i % rot]), stream)
     hbm("quantize_fp16_input", us, 3.0 * n * n, f"{n}x{n} fp16 -> E4M3, history 16")
     del x16
+    x32 = [x.float() for x in X]
+    us = time_launches(lambda i: ds.fp8_quantize(x32[i % rot], ds.E4M3, ring, out=Y[i % rot]), stream)
+    hbm("quantize_fp32_input", us, 5.0 * n * n, f"{n}x{n} fp32 -> E4M3, history 16")
+    del x32
     ws = ds.BiasGradWorkspace(n, n)
     gb = torch.empty(n, dtype=torch.bfloat16, device=dev)
-    us = time_launches(lambda: ds.fp8_bias_grad(x, out=gb, workspace=ws), stream)
+    us = time_launches(lambda i: ds.fp8_bias_grad(X[i % rot], out=gb, workspace=ws), stream)
     hbm("bias_grad", us, 2.0 * n * n + 2.0 * n, f"column sums of a {n}x{n} bf16 gradient, bf16 out")
-    a8 = torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev)
-    b8 = torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev)
-    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    del X, Y, YT
+    a8 = [torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    b8 = [torch.randint(0, 120, (n, n), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    c = [torch.empty((n, n), dtype=torch.bfloat16, device=dev) for _ in range(rot)]
     for name, layout in (("gemm_nn_dx", ds.NN), ("gemm_tn_dw", ds.TN)):
-        us = time_launches(lambda: ds.fp8_mm(a8, b8, ds.E5M2, ds.E4M3, layout, n, n, n, ring, ring, out=c), stream)
+        us = time_launches(lambda i: ds.fp8_mm(a8[i % rot], b8[i % rot], ds.E5M2, ds.E4M3, layout, n, n, n, ring,
+                                               ring, out=c[i % rot]), stream)
         tf = 2.0 * n ** 3 / (us * 1e-6) / 1e12
         out[name] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_FP8_TFLOPS, 4), "avg_launch_us": round(us, 2),
@@ -246,21 +257,19 @@ def main():
         r = i % rot
         if ev is not None:
             ev[0].record(stream)
-        ds.fp8_quantize(A[r], ds.E4M3, ring_a, out=A8[r])
+        # A and B in one launch, each with its own ring.
+        ds.fp8_quantize_batch([A[r], B[r]], ds.E4M3, [ring_a, ring_b], outs=[A8[r], B8[r]])
         if ev is not None:
             ev[1].record(stream)
-        ds.fp8_quantize(B[r], ds.E4M3, ring_b, out=B8[r])
-        if ev is not None:
-            ev[2].record(stream)
         ds.fp8_mm(A8[r], B8[r], ds.E4M3, ds.E4M3, ds.NT, n, n, n, ring_a, ring_b, out=C[r])
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -269,18 +278,18 @@ def main():
     t1 = time.perf_counter()
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    q_ms = [(e[0].elapsed_time(e[1]) + e[1].elapsed_time(e[2])) / 2 for e in events]
-    g_ms = [e[2].elapsed_time(e[3]) for e in events]
+    q_ms = [e[0].elapsed_time(e[1]) for e in events]
+    g_ms = [e[1].elapsed_time(e[2]) for e in events]
     q_avg = sum(q_ms) / len(q_ms)
     g_avg = sum(g_ms) / len(g_ms)
     flops = 2.0 * n * n * n
-    q_bytes = 3.0 * n * n
+    q_bytes = 6.0 * n * n       # two n x n bf16 tensors read, their codes written
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
     traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip"),
                                    "kernel_source_sha256", "hbm_bytes_per_launch")
     q_traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip"),
-                                     "quantize_source_sha256", "quantize_hbm_bytes_per_launch")
+                                     "quantize_source_sha256", "quantize_batch_hbm_bytes_per_launch")
 
     out = {
         "metric": "FP8 GEMM TFLOP/s (E4M3 NT 8192^3) + quantize GB/s, % of MI355X peak",
@@ -304,7 +313,8 @@ def main():
                      "avg_launch_us": round(g_avg * 1e3, 2)},
         "roofline_quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                               "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),
-                              "traffic": q_traffic, "kernel": "quantize_kernel<E4M3>",
+                              "traffic": q_traffic,
+                              "kernel": "quantize_batch_kernel<E4M3>: A and B, each with its ring, one launch",
                               "bytes_per_launch": q_bytes,
                               "avg_launch_us": round(q_avg * 1e3, 2)},
     }
@@ -322,7 +332,7 @@ def main():
             key = {"gemm_nn_dx": "gemm_nn", "gemm_tn_dw": "gemm_tn"}.get(name, name) + "_hbm_bytes_per_launch"
             if name == "quantize_dynamic":
                 a = traffic_from_profile(qsrc, sha_key, "amax_hbm_bytes_per_launch")
-                q = traffic_from_profile(qsrc, sha_key, "quantize_hbm_bytes_per_launch")
+                q = traffic_from_profile(qsrc, sha_key, "quantize_single_hbm_bytes_per_launch")
                 entry["traffic"] = None if a is None or q is None else a + q
             else:
                 entry["traffic"] = traffic_from_profile(src, sha_key, key)

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI in include/fp8ds.h):
     scale_ring_bytes(hist_len)
     scale_ring_init(ring, hist_len, fmt, init_scale=1.0)
     fp8_quantize(x, fmt, ring, out=None)             bf16 / fp16 / fp32 x
+    fp8_quantize_batch(xs, fmt, rings, ...)          several tensors, one launch
     fp8_quantize_2d(x, fmt, ring, layout, ...)       row-wise, transposed, dual
     fp8_quantize_dynamic(x, fmt, ring, out=None)     scale from x's own amax
     fp8_bias_grad(g, ..., out=None)                  column sums of a gradient
@@ -42,6 +43,14 @@ _lib = None
 
 class Fp8dsError(RuntimeError):
     pass
+
+
+MAX_BATCH = 8             # jobs of one fp8_quantize_batch call
+
+
+class _QuantJob(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("numel", ctypes.c_int64), ("ring", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("scale_inv_out", ctypes.c_void_p)]
 
 
 class _MmArgs(ctypes.Structure):
@@ -85,6 +94,8 @@ def lib():
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fp8_quantize_ex.restype = i32
         L.fp8_quantize_ex.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+        L.fp8_quantize_batch.restype = i32
+        L.fp8_quantize_batch.argtypes = [ctypes.POINTER(_QuantJob), i32, i32, i32, vp]
         L.fp8_quantize_2d.restype = i32
         L.fp8_quantize_2d.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
         L.fp8_quantize_dynamic.restype = i32
@@ -187,6 +198,28 @@ def fp8_quantize(x, fmt, ring, out=None, stream=None, max_blocks=None):
         _check(lib().fp8_quantize_ex(_ptr(x), x.numel(), in_type, int(fmt), _ptr(rbuf), _ptr(out),
                                      _stream(stream)))
     return out
+
+
+def fp8_quantize_batch(xs, fmt, rings, outs=None, scale_inv_outs=None, stream=None):
+    """Quantize several tensors of one input type, each with its own ring, in
+    one launch (each exactly as fp8_quantize).  scale_inv_outs: optional fp32
+    device tensors (or None entries) that receive each job's applied 1/scale.
+    Returns the list of code tensors."""
+    n = len(xs)
+    if n < 1 or n > MAX_BATCH or len(rings) != n:
+        raise Fp8dsError(f"fp8_quantize_batch takes 1..{MAX_BATCH} tensors and as many rings")
+    in_type = _in_type(xs[0])
+    if any(_in_type(x) != in_type for x in xs):
+        raise Fp8dsError("fp8_quantize_batch: all tensors must share one dtype")
+    if outs is None:
+        outs = [torch.empty(x.shape, dtype=torch.uint8, device=x.device) for x in xs]
+    sio = scale_inv_outs if scale_inv_outs is not None else [None] * n
+    jobs = (_QuantJob * n)()
+    for i in range(n):
+        jobs[i] = _QuantJob(xs[i].data_ptr(), xs[i].numel(), _ring_buf(rings[i]).data_ptr(), outs[i].data_ptr(),
+                            None if sio[i] is None else sio[i].data_ptr())
+    _check(lib().fp8_quantize_batch(jobs, n, in_type, int(fmt), _stream(stream)))
+    return outs
 
 
 def fp8_quantize_2d(x, fmt, ring, layout, out=None, out_t=None, stream=None):
@@ -312,6 +345,6 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
 
 
 __all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm",
-           "fp8_quantize", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad", "BiasGradWorkspace",
+           "fp8_quantize", "fp8_quantize_batch", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad", "BiasGradWorkspace",
            "bias_grad_workspace_bytes", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH",
            "IN_BF16", "IN_F16", "IN_F32", "ROWWISE", "TRANSPOSED", "DUAL"]

@@ -110,6 +110,32 @@ int fp8_quantize_ex(const void* x, int64_t numel, int in_type, int fmt, void* ri
   return launch_quantize(x, numel, in_type, fmt, ring, y_fp8, 0, static_cast<hipStream_t>(stream));
 }
 
+int fp8_quantize_batch(const fp8_quantize_job* jobs, int njobs, int in_type, int fmt, void* stream) {
+  const char* fn = "fp8_quantize_batch";
+  if (!jobs) return set_error(FP8DS_EINVAL, "%s: jobs is NULL", fn);
+  if (njobs < 1 || njobs > FP8DS_MAX_BATCH)
+    return set_error(FP8DS_EINVAL, "%s: njobs %d outside [1, %d]", fn, njobs, FP8DS_MAX_BATCH);
+  for (int i = 0; i < njobs; ++i) {
+    const fp8_quantize_job& j = jobs[i];
+    const int st = check_quantize(fn, j.x, j.numel, in_type, fmt, j.ring, j.y, 0);
+    if (st != FP8DS_OK) return st;
+    if ((reinterpret_cast<uintptr_t>(j.scale_inv_out) & 3u) != 0)
+      return set_error(FP8DS_EALIGN, "%s: job %d scale_inv_out not 4-byte aligned", fn, i);
+  }
+  for (int i = 0; i < njobs; ++i) {
+    for (int k = i + 1; k < njobs; ++k) {
+      const fp8_quantize_job &a = jobs[i], &b = jobs[k];
+      if (a.ring == b.ring) return set_error(FP8DS_EINVAL, "%s: jobs %d and %d share a ring", fn, i, k);
+      if (a.numel == 0 || b.numel == 0) continue;
+      if (overlaps(a.y, a.numel, b.y, b.numel) || overlaps(a.y, a.numel, b.x, b.numel * in_size(in_type)) ||
+          overlaps(b.y, b.numel, a.x, a.numel * in_size(in_type)))
+        return set_error(FP8DS_EINVAL, "%s: the output of job %d or %d overlaps the other job's input or output", fn,
+                         i, k);
+    }
+  }
+  return launch_quantize_batch(jobs, njobs, in_type, fmt, static_cast<hipStream_t>(stream));
+}
+
 int fp8_quantize_dynamic(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream) {
   const int st = check_quantize("fp8_quantize_dynamic", x, numel, in_type, fmt, ring, y_fp8, 0);
   if (st != FP8DS_OK || numel == 0) return st;

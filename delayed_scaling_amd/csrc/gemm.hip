@@ -643,15 +643,18 @@ GemmFn kernel_for(int tile, int layout, int fa, int fb) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Largest tile whose grid still fills the 256 CUs, else the one with most
-// tiles.  For the 256x256 size the eight-wave variant measured faster.
+// Tile choice by grid size, from per-shape timings on 256 CUs:
+//  * the eight-wave 256x256 tile when its grid fills the CUs;
+//  * else 128x128 when its grid fills them, or half-fills them with K >= 2048
+//    (a half-empty chip of 128x128 tiles beats a full one of 64x64 tiles once
+//    the K loop is long enough to amortize their higher per-tile rate);
+//  * else 64x64, the most tiles.
 int choose_tile(const GemmProblem& p) {
   constexpr int64_t kCUs = 256;
-  constexpr int order[] = {6, 1, 2};
-  for (int t : order) {
-    const int64_t tiles = cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch;
-    if (tiles >= kCUs) return t;
-  }
+  auto tiles = [&](int t) { return cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch; };
+  if (tiles(6) >= kCUs) return 6;
+  const int64_t t1 = tiles(1);
+  if (t1 >= kCUs || (2 * t1 >= kCUs && p.k >= 2048)) return 1;
   return 2;
 }
 

@@ -15,6 +15,10 @@ int check_launch(const char* kernel_name);
 int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStream_t stream);
 int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y, int max_blocks,
                     hipStream_t stream);
+}  // namespace fp8ds
+struct fp8_quantize_job;
+namespace fp8ds {
+int launch_quantize_batch(const fp8_quantize_job* jobs, int njobs, int in_type, int fmt, hipStream_t stream);
 int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, bool dual, void* ring, void* y,
                        void* y_t, int max_blocks, hipStream_t stream);
 int launch_amax(const void* x, int64_t numel, int in_type, int fmt, void* ring, hipStream_t stream);

@@ -20,6 +20,7 @@
 // top-level ticket finalizes the ring and every scratch word is back at zero
 // for the next call on the same stream.
 #include "device_common.h"
+#include "fp8ds.h"
 #include "launch.h"
 
 namespace fp8ds {
@@ -130,12 +131,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return v;
 }
 
-// Block-wide max; every thread gets the result.
+// Block-wide max, read by every thread after one barrier.  Each kernel calls
+// it once, at its end, so `red` needs no barrier before it is written.
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   v = wave_max(v);
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t r = red[0];
 #pragma unroll
@@ -144,20 +144,18 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
 }
 
 // Two-level completion tree, called by thread 0 of every block with the
-// block's max |x| as float32 bits.  Block b belongs to group b % kRingGroups;
-// each group has its own cache line holding a running max and a ticket.  All
-// words are device-scope atomics, performed where every XCD sees them.  A
-// ticket is taken only after the max it covers has been performed (its
-// returned value is waited for), so the block drawing a group's last ticket
-// reads a max that covers the whole group, and the block drawing the last
-// top-level ticket reads the max of all groups.  No release/acquire fence is
-// needed: nothing else a block wrote is read by the finalizing block, and an
-// agent-scope fence would write back the whole L2.  Returns true in exactly
-// one block, whose ring->amax_bits then holds the total.
-__device__ bool climb_tree(RingHeader* ring, uint32_t bmax) {
-  const int G = (int)gridDim.x;
+// block's max |x| as float32 bits; G blocks take part, this one is number b.
+// Block b belongs to group b % kRingGroups; each group has its own cache line
+// holding a running max and a ticket.  All words are device-scope atomics,
+// performed where every XCD sees them.  A ticket is taken only after the max
+// it covers has been performed (its returned value is waited for), so the
+// block drawing a group's last ticket reads a max that covers the whole
+// group, and the block drawing the last top-level ticket reads the max of all
+// groups.  No release/acquire fence is needed: the only data handed between
+// blocks are the atomic words themselves.
+__device__ bool climb_tree(RingHeader* ring, uint32_t bmax, int G, int b) {
   const int ngroups = G < kRingGroups ? G : kRingGroups;
-  const int g = (int)blockIdx.x % kRingGroups;
+  const int g = b % kRingGroups;
   const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);
   RingGroup* grp = ring_groups(ring) + g;
   const uint32_t prev = __hip_atomic_fetch_max(&grp->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -180,19 +178,24 @@ __device__ bool climb_tree(RingHeader* ring, uint32_t bmax) {
   return t2 == (uint32_t)ngroups - 1;
 }
 
-// Reduces the block's max, climbs the tree and, in the one last block,
-// returns true with *a = max |x| of the whole launch (float32 bits).  The
-// caller finalizes the ring and then calls clear_top().
-__device__ __forceinline__ bool fold_amax(RingHeader* ring, uint32_t amag_f32, uint32_t* red, int* s_last,
+// Called by every thread at the end of a launch of G blocks (this one number
+// b).  Reduces the block's max, climbs the tree and returns true in wave 0 of
+// the one block that finishes last, with *a = max |x| of the launch (float32
+// bits, the same in every lane).  Other waves, and other blocks, return false
+// and are done; the caller finalizes the ring with wave 0.
+__device__ __forceinline__ bool fold_amax(RingHeader* ring, uint32_t amag_f32, uint32_t* red, int G, int b,
                                           uint32_t* a) {
   const uint32_t bmax = block_max(amag_f32, red);
-  if (threadIdx.x == 0) *s_last = climb_tree(ring, bmax);
-  __syncthreads();
-  if (!*s_last) return false;
-  const uint32_t v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_returned(v);
-  *a = v;
-  return true;
+  if (threadIdx.x >= 64) return false;
+  uint32_t last = 0u, v = 0u;
+  if (threadIdx.x == 0 && climb_tree(ring, bmax, G, b)) {
+    v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(v);
+    last = 1u;
+  }
+  last = __builtin_amdgcn_readfirstlane(last);
+  *a = __builtin_amdgcn_readfirstlane(v);
+  return last != 0u;
 }
 
 __device__ __forceinline__ void clear_top(RingHeader* ring) {
@@ -200,54 +203,105 @@ __device__ __forceinline__ void clear_top(RingHeader* ring) {
   __hip_atomic_store(&ring->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The delayed-scaling ring update, run by the last block with the launch's
-// amax a: hist[idx] = a, idx advances, the next scale is FMAX over the
-// window's max when that is finite and positive and the quotient finite,
+// The ring as a launch finds it, read once at kernel start: the scale it
+// applies, the header, and in wave 0 the first 64 history entries other than
+// slot idx (lane j holds entry j, float32 bits, 0 for idx and past the end).
+// Nothing else writes the ring until the launch's last block finalizes it, so
+// that block needs no further loads for windows of up to 64 entries.
+struct RingPre {
+  float scale;
+  int hist_len, idx, fmt;
+  uint32_t win;
+};
+
+__device__ __forceinline__ bool header_ok(int H, int idx) {
+  return H >= 1 && H <= FP8DS_RING_MAX_HIST && idx >= 0 && idx < H;
+}
+
+__device__ __forceinline__ RingPre read_ring(RingHeader* ring) {
+  RingPre p;
+  p.scale = ring->scale;
+  p.hist_len = ring->hist_len;
+  p.idx = ring->idx;
+  p.fmt = ring->fmt;
+  p.win = 0u;
+  const int lane = (int)threadIdx.x;
+  if (lane < 64 && header_ok(p.hist_len, p.idx) && lane < p.hist_len && lane != p.idx)
+    p.win = __float_as_uint(ring_hist(ring)[lane]);
+  return p;
+}
+
+// The delayed-scaling ring update, run by wave 0 of the last block with the
+// launch's amax a: hist[idx] = a, idx advances, the next scale is FMAX over
+// the window's max when that is finite and positive and the quotient finite,
 // scale_inv_used = 1/scale (the scale this launch applied), amax_last = a.
+// scale_inv_out, when given, also receives 1/scale.
 template <int FMT>
-__device__ void finalize_ring(RingHeader* ring, uint32_t a, float scale, uint32_t* red) {
-  const int H = ring->hist_len;
-  const int idx = ring->idx;
-  const bool bad_header = H < 1 || H > 1024 || idx < 0 || idx >= H;
-  const bool fmt_mismatch = ring->fmt != FMT;
+__device__ void finalize_ring(RingHeader* ring, const RingPre& p, uint32_t a, float* scale_inv_out) {
+  const bool bad_header = !header_ok(p.hist_len, p.idx);
+  const bool fmt_mismatch = p.fmt != FMT;
   float* hist = ring_hist(ring);
-  uint32_t w = 0;
+  uint32_t w = max(p.win, a);
   if (!bad_header) {
-    for (int j = threadIdx.x; j < H; j += kQBlock) w = max(w, j == idx ? a : __float_as_uint(hist[j]));
+    for (int j = 64 + (int)threadIdx.x; j < p.hist_len; j += 64)
+      if (j != p.idx) w = max(w, __float_as_uint(hist[j]));
   }
-  w = block_max(w, red);
+  w = wave_max(w);
   if (threadIdx.x == 0) {
     if (bad_header || fmt_mismatch) {
       ring->status |= (bad_header ? kStatusBadHeader : 0u) | (fmt_mismatch ? kStatusFmtMismatch : 0u);
     } else {
-      hist[idx] = __uint_as_float(a);
-      ring->idx = idx + 1 == H ? 0 : idx + 1;
-      float next = scale;
+      hist[p.idx] = __uint_as_float(a);
+      ring->idx = p.idx + 1 == p.hist_len ? 0 : p.idx + 1;
+      float next = p.scale;
       if (w > 0u && w < 0x7F800000u) {
         const float t = FmtTraits<FMT>::kMax / __uint_as_float(w);
         if (__float_as_uint(t) < 0x7F800000u) next = t;
       }
       ring->scale = next;
-      ring->scale_inv_used = 1.0f / scale;
+      ring->scale_inv_used = 1.0f / p.scale;
       ring->amax_last = __uint_as_float(a);
     }
+    if (scale_inv_out != nullptr) *scale_inv_out = 1.0f / p.scale;
     clear_top(ring);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Row-wise quantize: x is a flat array of numel elements.
+// Row-wise quantize: x is a flat array of numel elements, nchunk whole 16-byte
+// chunks and `tail` elements after them.  One launch serves one tensor
+// (quantize_kernel) or up to kMaxBatch tensors with their own rings
+// (quantize_batch_kernel: consecutive runs of blocks per tensor, each run a
+// launch of its own as far as the tree is concerned).
 
+struct QuantJob {
+  const v4u* x;
+  uint8_t* y;
+  int64_t nchunk;
+  const uint8_t* x_tail;
+  uint8_t* y_tail;
+  int32_t tail;
+  int32_t blocks;            // blocks of this job (its grid)
+  RingHeader* ring;
+  float* scale_inv_out;      // optional copy of the applied 1/scale
+};
+
+constexpr int kMaxBatch = FP8DS_MAX_BATCH;
+struct QuantBatch {
+  QuantJob job[kMaxBatch];
+  int32_t njobs;
+};
+
+// Block b of a G-block grid over job j.
 template <int FMT, int IN>
-__global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict__ x, uint8_t* __restrict__ y,
-                                                           int64_t nchunk, const uint8_t* __restrict__ x_tail,
-                                                           uint8_t* __restrict__ y_tail, int tail,
-                                                           RingHeader* __restrict__ ring) {
+__device__ __forceinline__ void quantize_rows(const QuantJob& j, int G, int b, uint32_t* red) {
   using T = In<IN>;
   constexpr int kOut = T::kBits == 16 ? 8 : 4;   // codes per 16 input bytes
-  __shared__ uint32_t red[kQBlock / 64];
-  __shared__ int s_last;
-  const float scale = ring->scale;
+  const RingPre pre = read_ring(j.ring);
+  const float scale = pre.scale;
+  const v4u* __restrict__ x = j.x;
+  uint8_t* __restrict__ y = j.y;
+  const int64_t nchunk = j.nchunk;
   uint32_t amag = 0;
 
   auto put = [&](int64_t c, const uint32_t (&o)[2], bool stream) __attribute__((always_inline)) {
@@ -262,8 +316,8 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
       else *p = o[0];
     }
   };
-  const int64_t step = (int64_t)gridDim.x * kQBlock * kQUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
+  const int64_t step = (int64_t)G * kQBlock * kQUnroll;
+  for (int64_t base = (int64_t)b * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
     if (base + (kQUnroll - 1) * kQBlock < nchunk) {
       v4u v[kQUnroll];
 #pragma unroll
@@ -286,18 +340,35 @@ __global__ __launch_bounds__(kQBlock) void quantize_kernel(const v4u* __restrict
     }
   }
   // Elements past the last whole 16-byte chunk.
-  if (tail > 0 && blockIdx.x == 0 && threadIdx.x == 0) {
-    for (int i = 0; i < tail; ++i) {
+  if (j.tail > 0 && b == 0 && threadIdx.x == 0) {
+    for (int i = 0; i < j.tail; ++i) {
       uint32_t e[4] = {0u, 0u, 0u, 0u};
-      if constexpr (T::kBits == 16) e[0] = reinterpret_cast<const uint16_t*>(x_tail)[i];
-      else e[0] = reinterpret_cast<const uint32_t*>(x_tail)[i];
-      y_tail[i] = (uint8_t)(quant4<FMT, IN>(e, scale, amag) & 0xFFu);
+      if constexpr (T::kBits == 16) e[0] = reinterpret_cast<const uint16_t*>(j.x_tail)[i];
+      else e[0] = reinterpret_cast<const uint32_t*>(j.x_tail)[i];
+      j.y_tail[i] = (uint8_t)(quant4<FMT, IN>(e, scale, amag) & 0xFFu);
     }
   }
 
   uint32_t a;
-  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
-  finalize_ring<FMT>(ring, a, scale, red);
+  if (!fold_amax(j.ring, T::mag_f32(amag), red, G, b, &a)) return;
+  finalize_ring<FMT>(j.ring, pre, a, j.scale_inv_out);
+}
+
+template <int FMT, int IN>
+__global__ __launch_bounds__(kQBlock) void quantize_kernel(QuantJob job) {
+  __shared__ uint32_t red[kQBlock / 64];
+  quantize_rows<FMT, IN>(job, (int)gridDim.x, (int)blockIdx.x, red);
+}
+
+template <int FMT, int IN>
+__global__ __launch_bounds__(kQBlock) void quantize_batch_kernel(QuantBatch batch) {
+  __shared__ uint32_t red[kQBlock / 64];
+  int b = (int)blockIdx.x, j = 0;
+  while (j + 1 < batch.njobs && b >= batch.job[j].blocks) {
+    b -= batch.job[j].blocks;
+    ++j;
+  }
+  quantize_rows<FMT, IN>(batch.job[j], batch.job[j].blocks, b, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -326,8 +397,8 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
   __shared__ __attribute__((aligned(16))) char codes_lds[kTileR * kTileC];
   __shared__ __attribute__((aligned(16))) char trans_lds[kTileC * kTStride];
   __shared__ uint32_t red[kQBlock / 64];
-  __shared__ int s_last;
-  const float scale = ring->scale;
+  const RingPre pre = read_ring(ring);
+  const float scale = pre.scale;
   uint32_t amag = 0;
   lds_char_t* tile = (lds_char_t*)codes_lds;
   lds_char_t* ttile = (lds_char_t*)trans_lds;
@@ -405,8 +476,8 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
   }
 
   uint32_t a;
-  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
-  finalize_ring<FMT>(ring, a, scale, red);
+  if (!fold_amax(ring, T::mag_f32(amag), red, (int)gridDim.x, (int)blockIdx.x, &a)) return;
+  finalize_ring<FMT>(ring, pre, a, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,7 +493,7 @@ __global__ __launch_bounds__(kQBlock) void amax_kernel(const v4u* __restrict__ x
                                                        RingHeader* __restrict__ ring) {
   using T = In<IN>;
   __shared__ uint32_t red[kQBlock / 64];
-  __shared__ int s_last;
+  const RingPre pre = read_ring(ring);
   uint32_t amag = 0;
   auto take = [&](v4u v) __attribute__((always_inline)) {
     if constexpr (T::kBits == 16) {
@@ -453,11 +524,11 @@ __global__ __launch_bounds__(kQBlock) void amax_kernel(const v4u* __restrict__ x
     }
   }
   uint32_t a;
-  if (!fold_amax(ring, T::mag_f32(amag), red, &s_last, &a)) return;
+  if (!fold_amax(ring, T::mag_f32(amag), red, (int)gridDim.x, (int)blockIdx.x, &a)) return;
   if (threadIdx.x == 0) {
-    const bool bad = ring->hist_len != 1 || ring->idx != 0;
-    if (bad || ring->fmt != FMT) {
-      ring->status |= (bad ? kStatusBadHeader : 0u) | (ring->fmt != FMT ? kStatusFmtMismatch : 0u);
+    const bool bad = pre.hist_len != 1 || pre.idx != 0;
+    if (bad || pre.fmt != FMT) {
+      ring->status |= (bad ? kStatusBadHeader : 0u) | (pre.fmt != FMT ? kStatusFmtMismatch : 0u);
     } else {
       float s = 1.0f;
       if (a > 0u && a < 0x7F800000u) {
@@ -591,7 +662,8 @@ __global__ __launch_bounds__(256) void ring_init_kernel(RingHeader* ring, int hi
   }
 }
 
-typedef void (*QuantFn)(const v4u*, uint8_t*, int64_t, const uint8_t*, uint8_t*, int, RingHeader*);
+typedef void (*QuantFn)(QuantJob);
+typedef void (*QuantBatchFn)(QuantBatch);
 typedef void (*AmaxFn)(const v4u*, int64_t, const uint8_t*, int, RingHeader*);
 typedef void (*Quant2dFn)(const uint8_t*, uint8_t*, uint8_t*, int, int, int, RingHeader*);
 
@@ -599,6 +671,12 @@ template <int FMT>
 QuantFn quant_fn(int in) {
   return in == kInBf16 ? quantize_kernel<FMT, kInBf16> : in == kInF16 ? quantize_kernel<FMT, kInF16>
                                                                        : quantize_kernel<FMT, kInF32>;
+}
+template <int FMT>
+QuantBatchFn quant_batch_fn(int in) {
+  return in == kInBf16 ? quantize_batch_kernel<FMT, kInBf16>
+         : in == kInF16 ? quantize_batch_kernel<FMT, kInF16>
+                        : quantize_batch_kernel<FMT, kInF32>;
 }
 template <int FMT>
 AmaxFn amax_fn(int in) {
@@ -630,19 +708,50 @@ int launch_ring_init(void* ring, int hist_len, int fmt, float init_scale, hipStr
   return check_launch("ring_init_kernel");
 }
 
-int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y, int max_blocks,
-                    hipStream_t stream) {
-  const int eb = in_bytes(in_type);
-  const int per16 = 16 / eb;
-  const int64_t nchunk = numel / per16;
-  const int tail = (int)(numel % per16);
-  const int64_t blocks = stream_blocks(nchunk, max_blocks);
+namespace {
+
+// The job of one tensor on a grid of at most max_blocks blocks.
+QuantJob make_job(const void* x, int64_t numel, int in_type, void* ring, void* y, float* scale_inv_out,
+                  int max_blocks) {
+  const int per16 = 16 / in_bytes(in_type);
+  QuantJob j{};
+  j.nchunk = numel / per16;
+  j.tail = (int)(numel % per16);
+  j.blocks = (int)stream_blocks(j.nchunk, max_blocks);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   uint8_t* yb = static_cast<uint8_t*>(y);
+  j.x = reinterpret_cast<const v4u*>(xb);
+  j.y = yb;
+  j.x_tail = xb + j.nchunk * 16;
+  j.y_tail = yb + j.nchunk * per16;
+  j.ring = static_cast<RingHeader*>(ring);
+  j.scale_inv_out = scale_inv_out;
+  return j;
+}
+
+}  // namespace
+
+int launch_quantize(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y, int max_blocks,
+                    hipStream_t stream) {
+  const QuantJob j = make_job(x, numel, in_type, ring, y, nullptr, max_blocks);
   QuantFn fn = fmt == kE4M3 ? quant_fn<kE4M3>(in_type) : quant_fn<kE5M2>(in_type);
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kQBlock), 0, stream, reinterpret_cast<const v4u*>(xb), yb,
-                     nchunk, xb + nchunk * 16, yb + nchunk * per16, tail, static_cast<RingHeader*>(ring));
+  hipLaunchKernelGGL(fn, dim3((unsigned)j.blocks), dim3(kQBlock), 0, stream, j);
   return check_launch("quantize_kernel");
+}
+
+int launch_quantize_batch(const fp8_quantize_job* jobs, int njobs, int in_type, int fmt, hipStream_t stream) {
+  QuantBatch b{};
+  int64_t total = 0;
+  for (int i = 0; i < njobs; ++i) {
+    if (jobs[i].numel == 0) continue;
+    b.job[b.njobs] = make_job(jobs[i].x, jobs[i].numel, in_type, jobs[i].ring, jobs[i].y, jobs[i].scale_inv_out, 0);
+    total += b.job[b.njobs].blocks;
+    ++b.njobs;
+  }
+  if (b.njobs == 0) return 0;
+  QuantBatchFn fn = fmt == kE4M3 ? quant_batch_fn<kE4M3>(in_type) : quant_batch_fn<kE5M2>(in_type);
+  hipLaunchKernelGGL(fn, dim3((unsigned)total), dim3(kQBlock), 0, stream, b);
+  return check_launch("quantize_batch_kernel");
 }
 
 int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, bool dual, void* ring, void* y,

@@ -7,16 +7,18 @@ Forward   y  = X W^T (+ b):  X -> E4M3 (ring x), W -> E4M3 (ring w), NT GEMM.
 Backward  G -> E5M2 (ring g);  dX = G W (NN on the forward's W codes),
           dW = G^T X (TN on the forward's X codes), db = column sums of G
           (only when the bias needs a gradient).
-The forward's dequantization scales are copied aside when the forward runs
+The forward's dequantization scales are kept aside when the forward runs
 (fp8.py @f4c44ebf, forward-carries-scale entry), so a later forward on the
-same rings cannot change what the backward dequantizes with.  Every
-arithmetic step runs in the library's kernels; this module only allocates
-outputs and orders the calls on the current stream.
+same rings cannot change what the backward dequantizes with: X and W are
+quantized in one batched launch that also writes both applied 1/scale values
+into a small tensor the backward keeps.  Every arithmetic step runs in the
+library's kernels; this module only allocates outputs and orders the calls
+on the current stream.
 """
 import torch
 
 from . import (E4M3, E5M2, NN, NT, TN, BiasGradWorkspace, ScaleRing, bias_grad_workspace_bytes, fp8_bias_grad,
-               fp8_mm, fp8_quantize)
+               fp8_mm, fp8_quantize, fp8_quantize_batch)
 
 
 class Fp8LinearState:
@@ -35,21 +37,21 @@ class Fp8LinearState:
         return self.workspace
 
 
-def _scale_inv(ring):
-    """A copy of the ring's scale_inv_used (4 bytes at offset 4)."""
-    return ring.buf[4:8].clone()
-
-
 class _Fp8LinearFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, w, b, state):
         n_in = x.shape[-1]
         n_out = w.shape[0]
         x2 = x.reshape(-1, n_in).contiguous()
+        w2 = w.contiguous()
         t = x2.shape[0]
-        x8 = fp8_quantize(x2, E4M3, state.ring_x)
-        w8 = fp8_quantize(w.contiguous(), E4M3, state.ring_w)
-        sx, sw = _scale_inv(state.ring_x), _scale_inv(state.ring_w)
+        s = torch.empty(2, dtype=torch.float32, device=x.device)   # applied 1/scale of X and W
+        sx, sw = s[0:1], s[1:2]
+        if x2.dtype == w2.dtype:
+            x8, w8 = fp8_quantize_batch([x2, w2], E4M3, [state.ring_x, state.ring_w], scale_inv_outs=[sx, sw])
+        else:
+            x8, = fp8_quantize_batch([x2], E4M3, [state.ring_x], scale_inv_outs=[sx])
+            w8, = fp8_quantize_batch([w2], E4M3, [state.ring_w], scale_inv_outs=[sw])
         y = fp8_mm(x8, w8, E4M3, E4M3, NT, t, n_out, n_in, sx, sw, bias=b)
         ctx.save_for_backward(x8, w8, sx, sw)
         ctx.state = state

@@ -151,6 +151,30 @@ int fp8_quantize_with_grid(const void* x_bf16, int64_t numel, int fmt, void* rin
  * FP8DS_EINVAL. */
 int fp8_quantize_ex(const void* x, int64_t numel, int in_type, int fmt, void* ring, void* y_fp8, void* stream);
 
+/* Up to FP8DS_MAX_BATCH independent fp8_quantize_ex calls in one launch:
+ * each job is exactly fp8_quantize_ex on its own tensor and ring (fp8.py
+ * history @4dc5e923, ring-finalize entry, applied per job: each job's blocks
+ * elect their own last block).  Meant for the small tensors of one layer
+ * (X and W of a linear), where a launch is mostly fixed latency.
+ * All jobs share in_type and fmt.  Per job: x, numel, ring and y as in
+ * fp8_quantize_ex; scale_inv_out, if not NULL, a 4-byte aligned device fp32
+ * that receives fl32(1 / scale applied), the value the job's ring holds in
+ * scale_inv_used after the call, so the caller keeps the forward's
+ * dequantization scale without a copy.  Jobs with numel == 0 are skipped.
+ * jobs: host array of njobs entries (1 <= njobs <= FP8DS_MAX_BATCH), read
+ * before the call returns.  The rings must be distinct, and no job's y may
+ * overlap another job's x or y (FP8DS_EINVAL); per-job errors as
+ * fp8_quantize_ex, reported before anything is launched. */
+#define FP8DS_MAX_BATCH 8
+typedef struct fp8_quantize_job {
+  const void* x;
+  int64_t numel;
+  void* ring;
+  void* y;
+  float* scale_inv_out;
+} fp8_quantize_job;
+int fp8_quantize_batch(const fp8_quantize_job* jobs, int njobs, int in_type, int fmt, void* stream);
+
 /* Quantize of a rows x cols row-major tensor in one or two orientations
  * (history of `tests`: quantize / quantize_dual, orientations byte-equal to
  * the plain quantize):

@@ -124,3 +124,35 @@ def test_widened_entry_points_validate_before_launch(L):
     assert b"bias_scale_inv" in L.fp8_last_error()
     args.bias_kind = 5
     assert L.fp8_mm(ctypes.byref(args), None) == -1
+
+
+def test_batch_quantize_validates_before_launch(L):
+    v = ctypes.c_void_p
+    J = ds._QuantJob
+
+    def jobs(*js):
+        arr = (J * max(1, len(js)))()
+        for i, j in enumerate(js):
+            arr[i] = J(*j)
+        return arr
+
+    a = (1 << 20, 4096, 1 << 12, 1 << 24, None)          # x, numel, ring, y, scale_inv_out
+    b = (1 << 21, 4096, 1 << 13, 1 << 25, None)
+    assert L.fp8_quantize_batch(None, 1, 0, 0, None) == -1
+    assert L.fp8_quantize_batch(jobs(a), 0, 0, 0, None) == -1
+    assert L.fp8_quantize_batch(jobs(*([a] * 9)), 9, 0, 0, None) == -1
+    assert b"njobs" in L.fp8_last_error()
+    assert L.fp8_quantize_batch(jobs(a, b), 2, 3, 0, None) == -1                    # in_type
+    assert L.fp8_quantize_batch(jobs(a, b), 2, 0, 2, None) == -1                    # fmt
+    shared = (1 << 21, 4096, 1 << 12, 1 << 25, None)
+    assert L.fp8_quantize_batch(jobs(a, shared), 2, 0, 0, None) == -1
+    assert b"share a ring" in L.fp8_last_error()
+    y_on_x = (1 << 21, 4096, 1 << 13, 1 << 20, None)                                # b's y is a's x
+    assert L.fp8_quantize_batch(jobs(a, y_on_x), 2, 0, 0, None) == -1
+    assert b"overlaps" in L.fp8_last_error()
+    assert L.fp8_quantize_batch(jobs(a, (1 << 21, 4096, 1 << 13, 1 << 24, None)), 2, 0, 0, None) == -1   # same y
+    assert L.fp8_quantize_batch(jobs(a, (1 << 21, 4096, 1 << 13, 1 << 25, 1 << 26 | 2)), 2, 0, 0, None) == -2
+    assert L.fp8_quantize_batch(jobs((1 << 21, 4096, None, 1 << 25, None)), 1, 0, 0, None) == -3   # no ring
+    assert L.fp8_quantize_batch(jobs((1 << 21 | 8, 4096, 1 << 13, 1 << 25, None)), 1, 0, 0, None) == -2
+    empty = (None, 0, 1 << 14, None, None)
+    assert L.fp8_quantize_batch(jobs(empty, empty[:2] + (1 << 15,) + empty[3:]), 2, 0, 0, None) == 0   # nothing to do
