@@ -35,8 +35,10 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # The clocks settle after about 75 steps (40 ms) of this workload; fewer
+    # warm-up steps time part of the ramp.
+    ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--size", type=int, default=8192, help="M = N = K of the square workload")
     ap.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
