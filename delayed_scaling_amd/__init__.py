@@ -15,6 +15,7 @@ Entry points (same names as the C ABI in include/fp8ds.h):
     fp8_quantize_dynamic(x, fmt, ring, out=None)     scale from x's own amax
     fp8_bias_grad(g, ..., out=None)                  column sums of a gradient
     fp8_mm(a, b, ..., out=None)
+    fp8_mm_pair(first, second)                       two GEMMs, one launch for dX + dW
 plus ScaleRing (a ring in a torch uint8 device tensor), BiasGradWorkspace and
 read_ring().
 """
@@ -91,6 +92,8 @@ def lib():
         L.fp8_mm_with_tile.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm_with_grid.restype = ctypes.c_int
         L.fp8_mm_with_grid.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.fp8_mm_pair.restype = ctypes.c_int
+        L.fp8_mm_pair.argtypes = [ctypes.POINTER(_MmArgs), ctypes.POINTER(_MmArgs), ctypes.c_void_p]
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fp8_quantize_ex.restype = i32
         L.fp8_quantize_ex.argtypes = [vp, i64, i32, i32, vp, vp, vp]
@@ -297,18 +300,10 @@ def _addr(x):
     return ctypes.c_void_p(x.data_ptr())
 
 
-def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
-           batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
-           tile=None, max_workgroups=None, bias_fmt=None, bias_scale_inv=None, stream=None):
-    """C = bf16(A @ B * a_scale_inv * b_scale_inv + bias) on uint8 fp8 code tensors.
-
-    a, b: uint8 device tensors holding the stored operands (see include/fp8ds.h
-    for the NT/NN/TN storage); a_scale_inv / b_scale_inv: ScaleRing, fp32 device
-    tensor or device address; bias: bf16 or fp32 device tensor [n] or None.
-    Leading dimensions and batch strides default to the dense layout.
-    tile forces a tile of the family (TILES name or index); max_workgroups
-    bounds the grid so each workgroup runs several output tiles.
-    """
+def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
+             batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
+             bias_fmt=None, bias_scale_inv=None):
+    """The C argument struct of one GEMM, and its output tensor."""
     a_cols = m if layout == TN else k
     b_cols = k if layout == NT else n
     a_rows = k if layout == TN else m
@@ -336,6 +331,23 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
                    int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
                    int(stride_a), int(stride_b), int(stride_c),
                    _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias), _addr(bias_scale_inv))
+    return args, out
+
+
+def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
+           batch=1, lda=None, ldb=None, ldc=None, stride_a=None, stride_b=None, stride_c=None,
+           tile=None, max_workgroups=None, bias_fmt=None, bias_scale_inv=None, stream=None):
+    """C = bf16(A @ B * a_scale_inv * b_scale_inv + bias) on uint8 fp8 code tensors.
+
+    a, b: uint8 device tensors holding the stored operands (see include/fp8ds.h
+    for the NT/NN/TN storage); a_scale_inv / b_scale_inv: ScaleRing, fp32
+    device tensor or device address; bias: bf16 or fp32 device tensor [n] or None.
+    Leading dimensions and batch strides default to the dense layout.
+    tile forces a tile of the family (TILES name or index); max_workgroups
+    bounds the grid so each workgroup runs several output tiles.
+    """
+    args, out = _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias, out, batch, lda,
+                         ldb, ldc, stride_a, stride_b, stride_c, bias_fmt, bias_scale_inv)
     if tile is None and max_workgroups is None:
         _check(lib().fp8_mm(ctypes.byref(args), _stream(stream)))
     else:
@@ -344,7 +356,18 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
     return out
 
 
-__all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm",
+def fp8_mm_pair(first, second, stream=None):
+    """Two independent GEMMs issued together (one launch for an NN + TN pair in
+    the same formats, as a layer's dX and dW).  first / second: dicts of
+    fp8_mm's arguments (a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv,
+    b_scale_inv and optionally bias, out, ...).  Returns the two outputs."""
+    a0, out0 = _mm_args(**first)
+    a1, out1 = _mm_args(**second)
+    _check(lib().fp8_mm_pair(ctypes.byref(a0), ctypes.byref(a1), _stream(stream)))
+    return out0, out1
+
+
+__all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm", "fp8_mm_pair",
            "fp8_quantize", "fp8_quantize_batch", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad", "BiasGradWorkspace",
            "bias_grad_workspace_bytes", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH",
            "IN_BF16", "IN_F16", "IN_F32", "ROWWISE", "TRANSPOSED", "DUAL"]

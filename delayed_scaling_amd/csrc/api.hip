@@ -67,6 +67,89 @@ int64_t view_extent(int64_t rows, int64_t cols, int64_t ld) {
 }  // namespace
 }  // namespace fp8ds
 
+namespace fp8ds {
+namespace {
+
+int check_mm(const fp8_mm_args* a, GemmProblem* out, bool* empty) {
+  if (!a) return set_error(FP8DS_EINVAL, "fp8_mm: args is NULL");
+  if (!valid_fmt(a->fmt_a) || !valid_fmt(a->fmt_b)) return set_error(FP8DS_EINVAL, "fp8_mm: bad fmt_a/fmt_b");
+  if (a->layout < FP8DS_NT || a->layout > FP8DS_TN) return set_error(FP8DS_EINVAL, "fp8_mm: bad layout %d", a->layout);
+  if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_E5M2)
+    return set_error(FP8DS_EINVAL, "fp8_mm: bad bias_kind %d", a->bias_kind);
+  if ((a->bias_kind == FP8DS_BIAS_E4M3 || a->bias_kind == FP8DS_BIAS_E5M2) && !a->bias_scale_inv)
+    return set_error(FP8DS_EINVAL, "fp8_mm: an 8-bit bias needs bias_scale_inv");
+  const int64_t m = a->m, n = a->n, k = a->k, batch = a->batch == 0 ? 1 : a->batch;
+  if (m < 0 || n < 0 || k < 0 || batch < 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || batch > kMaxDim)
+    return set_error(FP8DS_EINVAL, "fp8_mm: dimensions must be in [0, 2^31)");
+  if (m == 0 || n == 0) {
+    *empty = true;
+    return FP8DS_OK;
+  }
+  const bool tn = a->layout == FP8DS_TN;
+  const int64_t a_rows = tn ? k : m, a_cols = tn ? m : k;
+  const int64_t b_rows = a->layout == FP8DS_NT ? n : k, b_cols = a->layout == FP8DS_NT ? k : n;
+  if (!a->c || !a->a_scale_inv || !a->b_scale_inv) return set_error(FP8DS_EINVAL, "fp8_mm: c or a scale pointer is NULL");
+  if (k > 0 && (!a->a || !a->b)) return set_error(FP8DS_EINVAL, "fp8_mm: a or b is NULL");
+  if (a->bias_kind != FP8DS_BIAS_NONE && !a->bias) return set_error(FP8DS_EINVAL, "fp8_mm: bias_kind set but bias is NULL");
+  if (a->lda < (k > 0 ? a_cols : 0) || a->ldb < (k > 0 ? b_cols : 0) || a->ldc < n)
+    return set_error(FP8DS_EINVAL, "fp8_mm: leading dimension smaller than the row length");
+  if (a->stride_a < 0 || a->stride_b < 0 || a->stride_c < 0) return set_error(FP8DS_EINVAL, "fp8_mm: negative stride");
+  if (batch > 1 && a->stride_c < m * a->ldc) return set_error(FP8DS_EINVAL, "fp8_mm: stride_c smaller than one output");
+  if ((k > 0 && (!aligned16(a->a) || !aligned16(a->b))) || !aligned16(a->c) ||
+      (a->bias_kind != FP8DS_BIAS_NONE && !aligned16(a->bias)))
+    return set_error(FP8DS_EALIGN, "fp8_mm: a, b, c and bias must be 16-byte aligned");
+  if ((a->lda & 15) || (a->ldb & 15) || (a->ldc & 7) || (a->stride_a & 15) || (a->stride_b & 15) ||
+      (a->stride_c & 7))
+    return set_error(FP8DS_EALIGN, "fp8_mm: lda, ldb, strides of a/b must be multiples of 16, ldc and stride_c of 8");
+  const int64_t ext_a = k > 0 ? view_extent(a_rows, a_cols, a->lda) : 0;
+  const int64_t ext_b = k > 0 ? view_extent(b_rows, b_cols, a->ldb) : 0;
+  if (ext_a >= 0x80000000LL || ext_b >= 0x80000000LL)
+    return set_error(FP8DS_EUNSUPPORTED, "fp8_mm: one batch entry of an operand spans 2 GiB or more");
+  GemmProblem p{};
+  p.a = static_cast<const uint8_t*>(a->a);
+  p.b = static_cast<const uint8_t*>(a->b);
+  p.c = static_cast<uint16_t*>(a->c);
+  p.fmt_a = a->fmt_a;
+  p.fmt_b = a->fmt_b;
+  p.layout = a->layout;
+  p.bias_kind = a->bias_kind;
+  p.m = (int)m;
+  p.n = (int)n;
+  p.k = (int)k;
+  p.batch = (int)batch;
+  p.lda = a->lda;
+  p.ldb = a->ldb;
+  p.ldc = a->ldc;
+  p.stride_a = a->stride_a;
+  p.stride_b = a->stride_b;
+  p.stride_c = a->stride_c;
+  p.extent_a = (uint32_t)ext_a;
+  p.extent_b = (uint32_t)ext_b;
+  p.a_scale_inv = a->a_scale_inv;
+  p.b_scale_inv = a->b_scale_inv;
+  p.bias = a->bias;
+  p.bias_scale_inv = a->bias_scale_inv;
+  *out = p;
+  return FP8DS_OK;
+}
+
+// Bytes from c that a problem's output spans, and likewise its operands
+// (stride 0 broadcasts span one entry) and its bias.
+int64_t mm_c_bytes(const GemmProblem& p) {
+  return ((int64_t)(p.batch - 1) * p.stride_c + (int64_t)(p.m - 1) * p.ldc + p.n) * 2;
+}
+int64_t mm_operand_bytes(uint32_t extent, const GemmProblem& p, bool is_b = false) {
+  if (p.k == 0) return 0;
+  return (int64_t)(p.batch - 1) * (is_b ? p.stride_b : p.stride_a) + extent;
+}
+int64_t mm_bias_bytes(const GemmProblem& p) {
+  const int64_t e = p.bias_kind == FP8DS_BIAS_F32 ? 4 : p.bias_kind == FP8DS_BIAS_BF16 ? 2 : 1;
+  return p.n * e;
+}
+
+}  // namespace
+}  // namespace fp8ds
+
 using namespace fp8ds;
 
 extern "C" {
@@ -202,63 +285,35 @@ int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_grid(a, -1, 
 int fp8_mm_with_tile(const fp8_mm_args* a, int tile, void* stream) { return fp8_mm_with_grid(a, tile, 0, stream); }
 
 int fp8_mm_with_grid(const fp8_mm_args* a, int tile, int max_workgroups, void* stream) {
-  if (!a) return set_error(FP8DS_EINVAL, "fp8_mm: args is NULL");
   if (max_workgroups < 0) return set_error(FP8DS_EINVAL, "fp8_mm: max_workgroups %d < 0", max_workgroups);
-  if (!valid_fmt(a->fmt_a) || !valid_fmt(a->fmt_b)) return set_error(FP8DS_EINVAL, "fp8_mm: bad fmt_a/fmt_b");
-  if (a->layout < FP8DS_NT || a->layout > FP8DS_TN) return set_error(FP8DS_EINVAL, "fp8_mm: bad layout %d", a->layout);
-  if (a->bias_kind < FP8DS_BIAS_NONE || a->bias_kind > FP8DS_BIAS_E5M2)
-    return set_error(FP8DS_EINVAL, "fp8_mm: bad bias_kind %d", a->bias_kind);
-  if ((a->bias_kind == FP8DS_BIAS_E4M3 || a->bias_kind == FP8DS_BIAS_E5M2) && !a->bias_scale_inv)
-    return set_error(FP8DS_EINVAL, "fp8_mm: an 8-bit bias needs bias_scale_inv");
-  const int64_t m = a->m, n = a->n, k = a->k, batch = a->batch == 0 ? 1 : a->batch;
-  if (m < 0 || n < 0 || k < 0 || batch < 0 || m > kMaxDim || n > kMaxDim || k > kMaxDim || batch > kMaxDim)
-    return set_error(FP8DS_EINVAL, "fp8_mm: dimensions must be in [0, 2^31)");
-  if (m == 0 || n == 0) return FP8DS_OK;
-  const bool tn = a->layout == FP8DS_TN;
-  const int64_t a_rows = tn ? k : m, a_cols = tn ? m : k;
-  const int64_t b_rows = a->layout == FP8DS_NT ? n : k, b_cols = a->layout == FP8DS_NT ? k : n;
-  if (!a->c || !a->a_scale_inv || !a->b_scale_inv) return set_error(FP8DS_EINVAL, "fp8_mm: c or a scale pointer is NULL");
-  if (k > 0 && (!a->a || !a->b)) return set_error(FP8DS_EINVAL, "fp8_mm: a or b is NULL");
-  if (a->bias_kind != FP8DS_BIAS_NONE && !a->bias) return set_error(FP8DS_EINVAL, "fp8_mm: bias_kind set but bias is NULL");
-  if (a->lda < (k > 0 ? a_cols : 0) || a->ldb < (k > 0 ? b_cols : 0) || a->ldc < n)
-    return set_error(FP8DS_EINVAL, "fp8_mm: leading dimension smaller than the row length");
-  if (a->stride_a < 0 || a->stride_b < 0 || a->stride_c < 0) return set_error(FP8DS_EINVAL, "fp8_mm: negative stride");
-  if (batch > 1 && a->stride_c < m * a->ldc) return set_error(FP8DS_EINVAL, "fp8_mm: stride_c smaller than one output");
-  if ((k > 0 && (!aligned16(a->a) || !aligned16(a->b))) || !aligned16(a->c) ||
-      (a->bias_kind != FP8DS_BIAS_NONE && !aligned16(a->bias)))
-    return set_error(FP8DS_EALIGN, "fp8_mm: a, b, c and bias must be 16-byte aligned");
-  if ((a->lda & 15) || (a->ldb & 15) || (a->ldc & 7) || (a->stride_a & 15) || (a->stride_b & 15) ||
-      (a->stride_c & 7))
-    return set_error(FP8DS_EALIGN, "fp8_mm: lda, ldb, strides of a/b must be multiples of 16, ldc and stride_c of 8");
-  const int64_t ext_a = k > 0 ? view_extent(a_rows, a_cols, a->lda) : 0;
-  const int64_t ext_b = k > 0 ? view_extent(b_rows, b_cols, a->ldb) : 0;
-  if (ext_a >= 0x80000000LL || ext_b >= 0x80000000LL)
-    return set_error(FP8DS_EUNSUPPORTED, "fp8_mm: one batch entry of an operand spans 2 GiB or more");
   GemmProblem p{};
-  p.a = static_cast<const uint8_t*>(a->a);
-  p.b = static_cast<const uint8_t*>(a->b);
-  p.c = static_cast<uint16_t*>(a->c);
-  p.fmt_a = a->fmt_a;
-  p.fmt_b = a->fmt_b;
-  p.layout = a->layout;
-  p.bias_kind = a->bias_kind;
-  p.m = (int)m;
-  p.n = (int)n;
-  p.k = (int)k;
-  p.batch = (int)batch;
-  p.lda = a->lda;
-  p.ldb = a->ldb;
-  p.ldc = a->ldc;
-  p.stride_a = a->stride_a;
-  p.stride_b = a->stride_b;
-  p.stride_c = a->stride_c;
-  p.extent_a = (uint32_t)ext_a;
-  p.extent_b = (uint32_t)ext_b;
-  p.a_scale_inv = a->a_scale_inv;
-  p.b_scale_inv = a->b_scale_inv;
-  p.bias = a->bias;
-  p.bias_scale_inv = a->bias_scale_inv;
+  bool empty = false;
+  if (const int st = check_mm(a, &p, &empty)) return st;
+  if (empty) return FP8DS_OK;
   return launch_gemm(p, tile, max_workgroups, static_cast<hipStream_t>(stream));
+}
+
+int fp8_mm_pair(const fp8_mm_args* first, const fp8_mm_args* second, void* stream) {
+  GemmProblem p[2]{};
+  bool empty[2] = {false, false};
+  if (const int st = check_mm(first, &p[0], &empty[0])) return st;
+  if (const int st = check_mm(second, &p[1], &empty[1])) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (empty[0] || empty[1]) {
+    if (!empty[0]) return launch_gemm(p[0], -1, 0, s);
+    if (!empty[1]) return launch_gemm(p[1], -1, 0, s);
+    return FP8DS_OK;
+  }
+  // Each output may be written while the other problem reads its operands.
+  for (int i = 0; i < 2; ++i) {
+    const GemmProblem &w = p[i], &r = p[1 - i];
+    const int64_t c_bytes = mm_c_bytes(w);
+    if (overlaps(w.c, c_bytes, r.c, mm_c_bytes(r)) || overlaps(w.c, c_bytes, r.a, mm_operand_bytes(r.extent_a, r)) ||
+        overlaps(w.c, c_bytes, r.b, mm_operand_bytes(r.extent_b, r, true)) ||
+        (r.bias_kind != FP8DS_BIAS_NONE && overlaps(w.c, c_bytes, r.bias, mm_bias_bytes(r))))
+      return set_error(FP8DS_EINVAL, "fp8_mm_pair: the output of one problem overlaps an input or the output of the other");
+  }
+  return launch_gemm_pair(p[0], p[1], s);
 }
 
 }  // extern "C"

@@ -320,8 +320,9 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TN][TM]) {
     for (int j = 0; j < TM; ++j) acc[i][j] = v16f{};
 }
 
-// Global -> LDS side of a workgroup that runs the output tiles blockIdx.x,
-// blockIdx.x + G, ... (G = grid size) as one stream of K stages of kBK bytes.
+// Global -> LDS side of a workgroup that runs the output tiles wg, wg + G,
+// ... (wg its index among the G workgroups of its problem) as one stream of K
+// stages of kBK bytes.
 // Stage s lands in LDS buffer s % kStages as [A tile | B tile]; each of the
 // NW waves brings 1 KiB per buffer_load ... lds.  The next stage to issue is
 // stage k of the workgroup's tile number it.  Each tile's operand strips get
@@ -337,7 +338,7 @@ struct TileLoader {
   static constexpr int LPS = A_LOADS + B_LOADS;   // loads per wave and stage
   static_assert(A_LOADS >= 1 && B_LOADS >= 1, "tile too small");
 
-  int it = 0, k = 0;
+  int it = 0, k = 0, wg = 0, G = 1;
   uint32_t s = 0;
   v4i ra, rb;
   uint32_t a_voff[A_LOADS], b_voff[B_LOADS];
@@ -364,7 +365,9 @@ struct TileLoader {
       b_voff[j] = slot_offset<B_KC, BN>((j * NW + wave) * 64 + lane, n0, p.n, p.ldb);
   }
 
-  __device__ __forceinline__ void init(const GemmKArgs& p, int wave, int lane, int kt_full) {
+  __device__ __forceinline__ void init(const GemmKArgs& p, int wave, int lane, int kt_full, int wg_, int G_) {
+    wg = wg_;
+    G = G_;
     // The same for every tile, as all tiles share K.
 #pragma unroll
     for (int j = 0; j < A_LOADS; ++j)
@@ -373,7 +376,7 @@ struct TileLoader {
     for (int j = 0; j < B_LOADS; ++j)
       tail_oob |= (uint32_t)(slot_kpos<B_KC, BN>((j * NW + wave) * 64 + lane) >= p.k - kt_full * kBK)
                   << (A_LOADS + j);
-    set_tile(p, blockIdx.x, wave, lane);
+    set_tile(p, wg, wave, lane);
   }
 
   // Scalar part of the next stage's loads: K offsets and LDS bases.
@@ -401,7 +404,7 @@ struct TileLoader {
     if (++k == kt_total) {
       k = 0;
       if (++it < my_tiles) {
-        set_tile(p, blockIdx.x + it * gridDim.x, wave, lane);
+        set_tile(p, wg + it * G, wave, lane);
       } else {
         ra[2] = 0;
         rb[2] = 0;
@@ -461,16 +464,19 @@ __device__ __forceinline__ void mfmas(v16f (&acc)[TN][TM], const v8i (&fa)[TM], 
 // each own a (BM/WGM) x (BN/WGN) block of the tile.  Every wave runs all
 // stages: wait for stage s+1, barrier, then stage s's MFMAs interleaved with
 // the loads of stage s+kStages and the LDS reads of stage s+1's fragments.
-template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC, bool B_KC, int FA, int FB>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
+template <int BM, int BN, int kStages>
+constexpr int smem_bytes() { return kStages * (BM + BN) * kBK; }
+
+// Workgroup wg of the G that run one problem (a whole launch, or one part of
+// a launch shared by two problems); smem: the workgroup's LDS stages.
+template <int BM, int BN, int WGM, int WGN, int kStages, bool A_KC, bool B_KC, int FA, int FB>
+__device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, int wg, int G) {
   constexpr int NW = WGM * WGN, kThreads = 64 * NW;   // waves in a WGM x WGN grid
   constexpr int WM = BM / WGM, WN = BN / WGN;          // C block of one wave
   constexpr int TM = WM / 32, TN = WN / 32;
   using Loader = TileLoader<BM, BN, NW, kStages, A_KC, B_KC>;
   constexpr int STAGE = Loader::STAGE, LPS = Loader::LPS;
   static_assert(TM >= 1 && TN >= 1, "tile too small");
-  __shared__ __attribute__((aligned(1024))) char smem_raw[kStages * STAGE];
-  lds_char_t* smem = (lds_char_t*)smem_raw;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -479,26 +485,30 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
   // The loads of a tile's first stages go out while the previous tile's last
   // stages compute, so the operand pipeline never drains between tiles and
   // the epilogue's stores overlap the loads.
-  const int G = gridDim.x;
   const int total = p.tiles_m * p.tiles_n * p.batch;
-  const int my_tiles = (total - 1 - (int)blockIdx.x) / G + 1;
+  const int my_tiles = (total - 1 - wg) / G + 1;     // >= 1: launches keep G <= total
   const int kt_total = (p.k + kBK - 1) / kBK;
   const int kt_full = p.k / kBK;
   const bool kfix = (p.k & 15) != 0;
 
-  // The dequantization factor, read before any operand load is in flight.
-  const float alpha = __builtin_bit_cast(
-      float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, p.a_scale_inv[0] * p.b_scale_inv[0])));
+  // The dequantization scales: scalar loads, issued now and first waited for
+  // after the prologue's operand loads are in flight (they count on lgkmcnt,
+  // so no later wait for them holds back an operand load).
+  const float sa_inv = p.a_scale_inv[0], sb_inv = p.b_scale_inv[0];
+  auto make_alpha = [&]() __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, sa_inv * sb_inv)));
+  };
 
   v16f acc[TN][TM];
   zero_acc(acc);
   if (kt_total == 0) {          // K = 0: every output is bf16(bias) or zero
-    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane, alpha);
+    const float alpha = make_alpha();
+    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, wg + it * G, r0, c0, lane, alpha);
     return;
   }
 
   Loader ld;
-  ld.init(p, wave, lane, kt_full);
+  ld.init(p, wave, lane, kt_full, wg, G);
   auto buf = [&](uint32_t st) __attribute__((always_inline)) { return smem + (st % kStages) * STAGE; };
 
   // Stage s+1 is visible to the whole workgroup: zero its K padding first if
@@ -556,6 +566,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
   // Prologue: stages 0 .. kStages-1 in flight, stage 0's fragments in set 0.
 #pragma unroll
   for (int st = 0; st < kStages; ++st) ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
+  const float alpha = make_alpha();
   wait_stages<LPS, kStages>(kStages - 1);
   lds_barrier();
   if (kfix && kt_full == 0) {
@@ -587,13 +598,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
       stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
     }
     stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
-    store_c_tile<BM, BN>(p, acc, blockIdx.x + it * G, r0, c0, lane, alpha);
+    store_c_tile<BM, BN>(p, acc, wg + it * G, r0, c0, lane, alpha);
     zero_acc(acc);
     read_frags<BM, BN, TM, TN, A_KC, B_KC>(buf(s0 + kt_total), r0, c0, lane, fa0, fb0);
   }
   // The loads of the stages past the last tile write this workgroup's LDS:
   // let them land before the workgroup ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// One problem per launch: workgroup blockIdx.x of gridDim.x.
+template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC, bool B_KC, int FA, int FB>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, kStages>()];
+  gemm_body<BM, BN, WGM, WGN, kStages, A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x,
+                                                          (int)gridDim.x);
+}
+
+// Two independent problems in one launch (a layer's dX and dW): workgroups
+// [0, g0) run the first, the rest the second, each as a grid of its own.  The
+// two share the tile, the formats and the LDS of a workgroup; only the
+// operand orientations differ.  g0 is a multiple of 8 whenever the first
+// problem's workgroups run more than one tile each, so the second keeps the
+// tile-to-XCD mapping of a launch of its own.
+template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1,
+          int FA, int FB>
+__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_pair_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, kStages>()];
+  const int wg = (int)blockIdx.x;
+  if (wg < g0)
+    gemm_body<BM, BN, WGM, WGN, kStages, A_KC0, B_KC0, FA, FB>(p0, (lds_char_t*)smem_raw, wg, g0);
+  else
+    gemm_body<BM, BN, WGM, WGN, kStages, A_KC1, B_KC1, FA, FB>(p1, (lds_char_t*)smem_raw, wg - g0,
+                                                              (int)gridDim.x - g0);
 }
 
 // ---------------------------------------------------------------------------
@@ -629,6 +666,25 @@ GemmFn pick_kernel(int layout, int fa, int fb) {
 
 #undef FP8DS_FMT_CASES
 
+// The fused pair: a layer's dX (NN) and dW (TN), same formats, tiles 1, 2, 6.
+typedef void (*GemmPairFn)(GemmKArgs, GemmKArgs, int);
+
+template <int BM, int BN, int WGM, int WGN, int ST, int OCC>
+GemmPairFn pick_pair_kernel(int fa, int fb) {
+  if (fa == 0 && fb == 0) return gemm_pair_kernel<BM, BN, WGM, WGN, ST, OCC, true, false, false, false, 0, 0>;
+  if (fa == 1 && fb == 0) return gemm_pair_kernel<BM, BN, WGM, WGN, ST, OCC, true, false, false, false, 1, 0>;
+  if (fa == 0 && fb == 1) return gemm_pair_kernel<BM, BN, WGM, WGN, ST, OCC, true, false, false, false, 0, 1>;
+  return gemm_pair_kernel<BM, BN, WGM, WGN, ST, OCC, true, false, false, false, 1, 1>;
+}
+
+GemmPairFn pair_kernel_for(int tile, int fa, int fb) {
+  switch (tile) {
+    case 1: return pick_pair_kernel<128, 128, 2, 2, 4, 2>(fa, fb);
+    case 2: return pick_pair_kernel<64, 64, 2, 2, 4, 4>(fa, fb);
+    default: return pick_pair_kernel<256, 256, 4, 2, 4, 1>(fa, fb);
+  }
+}
+
 GemmFn kernel_for(int tile, int layout, int fa, int fb) {
   switch (tile) {
     case 0: return pick_kernel<256, 256, 2, 2, 4, 1>(layout, fa, fb);
@@ -649,27 +705,41 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    (a half-empty chip of 128x128 tiles beats a full one of 64x64 tiles once
 //    the K loop is long enough to amortize their higher per-tile rate);
 //  * else 64x64, the most tiles.
-int choose_tile(const GemmProblem& p) {
+int64_t tile_count(const GemmProblem& p, int t) {
+  return cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch;
+}
+
+// The rule over a launch's total tile count and (shortest) K.
+int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k) {
   constexpr int64_t kCUs = 256;
-  auto tiles = [&](int t) { return cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch; };
-  if (tiles(6) >= kCUs) return 6;
-  const int64_t t1 = tiles(1);
-  if (t1 >= kCUs || (2 * t1 >= kCUs && p.k >= 2048)) return 1;
+  if (count(ps, 6) >= kCUs) return 6;
+  const int64_t t1 = count(ps, 1);
+  if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 1;
   return 2;
+}
+
+int choose_tile(const GemmProblem& p) {
+  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k);
+}
+
+// For a fused pair: the same rule over both problems' tiles and the shorter K.
+int choose_pair_tile(const GemmProblem (&pp)[2]) {
+  return tile_for([](const GemmProblem* q, int t) { return tile_count(q[0], t) + tile_count(q[1], t); }, pp,
+                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k);
 }
 
 // Workgroups of one kernel that fit on the device at once (CUs x occupancy),
 // cached per device and kernel.
-int resident_workgroups(GemmFn fn, int slot, int threads) {
+int resident_workgroups(const void* fn, int slot, int threads) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices][kNumTiles * 12];
+  static std::atomic<int> cache[kMaxDevices][kNumTiles * 16];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
   const int hit = cache[dev][slot].load(std::memory_order_relaxed);
   if (hit > 0) return hit;
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), threads, 0) !=
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0) !=
           hipSuccess)
     return 0;
   const int r = cus * per_cu;
@@ -679,8 +749,9 @@ int resident_workgroups(GemmFn fn, int slot, int threads) {
 
 }  // namespace
 
-int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hipStream_t stream) {
-  const int t = (tile_override >= 0 && tile_override < kNumTiles) ? tile_override : choose_tile(p);
+namespace {
+
+GemmKArgs make_kargs(const GemmProblem& p, int t) {
   GemmKArgs k{};
   k.a = p.a;
   k.b = p.b;
@@ -706,20 +777,72 @@ int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hip
   k.bias_scale_inv = p.bias_scale_inv;
   k.bias_kind = p.bias_kind;
   k.ldc_small = p.ldc * 256 < 0x80000000LL;
+  return k;
+}
+
+// Workgroups for `total` tiles given `g` resident slots: one per slot, each
+// running every G-th tile; G a multiple of 8 keeps tile v on XCD v mod 8.
+int64_t grid_for(int64_t total, int64_t g) {
+  if (g <= 0) g = total;
+  if (g < total && g >= 8) g &= ~int64_t(7);
+  return g > total ? total : g;
+}
+
+int check_counts(int64_t total, int64_t g, int k) {
+  if (total > 0x7FFFFFFF) return set_error(-3, "fp8_mm: %lld tiles exceed the grid limit", (long long)total);
+  if (cdiv(total, g) * cdiv(k, 64) > 0x7FFFFFFF)
+    return set_error(-3, "fp8_mm: %lld K stages per workgroup exceed the kernel's counter",
+                     (long long)(cdiv(total, g) * cdiv(k, 64)));
+  return 0;
+}
+
+}  // namespace
+
+int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hipStream_t stream) {
+  const int t = (tile_override >= 0 && tile_override < kNumTiles) ? tile_override : choose_tile(p);
+  const GemmKArgs k = make_kargs(p, t);
   const int64_t total = (int64_t)k.tiles_m * k.tiles_n * k.batch;
   if (total > 0x7FFFFFFF) return set_error(-3, "fp8_mm: %lld tiles exceed the grid limit", (long long)total);
   GemmFn fn = kernel_for(t, p.layout, p.fmt_a, p.fmt_b);
   const int threads = 64 * kTiles[t].waves;
-  // One workgroup per resident slot, each running every G-th tile; G a
-  // multiple of 8 keeps tile v on XCD v mod 8.
-  int64_t g = max_workgroups > 0 ? max_workgroups : resident_workgroups(fn, t * 12 + p.layout * 4 + p.fmt_a * 2 + p.fmt_b, threads);
-  if (g <= 0) g = total;
-  if (g < total && g >= 8) g &= ~int64_t(7);
-  if (g > total) g = total;
-  if (cdiv(total, g) * cdiv(p.k, 64) > 0x7FFFFFFF)
-    return set_error(-3, "fp8_mm: %lld K stages per workgroup exceed the kernel's counter", (long long)(cdiv(total, g) * cdiv(p.k, 64)));
+  const int64_t g = grid_for(total, max_workgroups > 0
+                                        ? max_workgroups
+                                        : resident_workgroups(reinterpret_cast<const void*>(fn),
+                                                              t * 16 + p.layout * 4 + p.fmt_a * 2 + p.fmt_b, threads));
+  if (const int st = check_counts(total, g, p.k)) return st;
   hipLaunchKernelGGL(fn, dim3((unsigned)g), dim3(threads), 0, stream, k);
   return check_launch("gemm_kernel");
+}
+
+int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
+  if (!(p0.layout == 1 && p1.layout == 2 && p0.fmt_a == p1.fmt_a && p0.fmt_b == p1.fmt_b)) {
+    const int st = launch_gemm(p0, -1, 0, stream);
+    return st ? st : launch_gemm(p1, -1, 0, stream);
+  }
+  const GemmProblem pp[2] = {p0, p1};
+  const int t = choose_pair_tile(pp);
+  const GemmKArgs k0 = make_kargs(p0, t), k1 = make_kargs(p1, t);
+  const int64_t n0 = (int64_t)k0.tiles_m * k0.tiles_n * k0.batch, n1 = (int64_t)k1.tiles_m * k1.tiles_n * k1.batch;
+  if (n0 > 0x7FFFFFFF || n1 > 0x7FFFFFFF) return set_error(-3, "fp8_mm_pair: tiles exceed the grid limit");
+  GemmPairFn fn = pair_kernel_for(t, p0.fmt_a, p0.fmt_b);
+  const int threads = 64 * kTiles[t].waves;
+  const int64_t res = resident_workgroups(reinterpret_cast<const void*>(fn), t * 16 + 12 + p0.fmt_a * 2 + p0.fmt_b,
+                                          threads);
+  // Both problems' tiles at once when the device holds them all; otherwise the
+  // resident slots split in proportion to each problem's MFMA work.
+  int64_t g0 = n0, g1 = n1;
+  if (res > 0 && n0 + n1 > res) {
+    const double w0 = (double)n0 * (p0.k > 0 ? p0.k : 1), w1 = (double)n1 * (p1.k > 0 ? p1.k : 1);
+    int64_t s0 = (int64_t)((double)res * w0 / (w0 + w1) + 0.5);
+    if (s0 < 1) s0 = 1;
+    if (s0 > res - 1) s0 = res - 1;
+    g0 = grid_for(n0, s0);
+    g1 = grid_for(n1, res - g0);
+  }
+  if (const int st = check_counts(n0, g0, p0.k)) return st;
+  if (const int st = check_counts(n1, g1, p1.k)) return st;
+  hipLaunchKernelGGL(fn, dim3((unsigned)(g0 + g1)), dim3(threads), 0, stream, k0, k1, (int)g0);
+  return check_launch("gemm_pair_kernel");
 }
 
 }  // namespace fp8ds

@@ -45,4 +45,8 @@ struct GemmProblem {
 // workgroups the device holds at once.
 int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hipStream_t stream);
 
+// Two independent problems; one launch when p0 is NN and p1 TN in the same
+// formats (a layer's dX and dW), else two launches in order.
+int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream);
+
 }  // namespace fp8ds

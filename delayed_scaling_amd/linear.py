@@ -4,9 +4,9 @@ the layer's forward and backward live in one autograd Function whose backward
 reads only what the forward saved, so it runs in FP8 wherever it is called).
 
 Forward   y  = X W^T (+ b):  X -> E4M3 (ring x), W -> E4M3 (ring w), NT GEMM.
-Backward  G -> E5M2 (ring g);  dX = G W (NN on the forward's W codes),
-          dW = G^T X (TN on the forward's X codes), db = column sums of G
-          (only when the bias needs a gradient).
+Backward  G -> E5M2 (ring g);  dX = G W (NN on the forward's W codes) and
+          dW = G^T X (TN on the forward's X codes) in one launch, db = column
+          sums of G (only when the bias needs a gradient).
 The forward's dequantization scales are kept aside when the forward runs
 (fp8.py @f4c44ebf, forward-carries-scale entry), so a later forward on the
 same rings cannot change what the backward dequantizes with: X and W are
@@ -18,7 +18,7 @@ on the current stream.
 import torch
 
 from . import (E4M3, E5M2, NN, NT, TN, BiasGradWorkspace, ScaleRing, bias_grad_workspace_bytes, fp8_bias_grad,
-               fp8_mm, fp8_quantize, fp8_quantize_batch)
+               fp8_mm, fp8_mm_pair, fp8_quantize, fp8_quantize_batch)
 
 
 class Fp8LinearState:
@@ -68,10 +68,17 @@ class _Fp8LinearFn(torch.autograd.Function):
         g2 = gy.reshape(-1, n_out).to(torch.bfloat16).contiguous()
         g8 = fp8_quantize(g2, E5M2, state.ring_g)
         dx = dw = db = None
-        if ctx.needs_input_grad[0]:
-            dx = fp8_mm(g8, w8, E5M2, E4M3, NN, t, n_in, n_out, state.ring_g, sw).view(ctx.x_shape)
-        if ctx.needs_input_grad[1]:
-            dw = fp8_mm(g8, x8, E5M2, E4M3, TN, n_out, n_in, t, state.ring_g, sx).view(n_out, n_in)
+        dx_args = dict(a=g8, b=w8, fmt_a=E5M2, fmt_b=E4M3, layout=NN, m=t, n=n_in, k=n_out,
+                       a_scale_inv=state.ring_g, b_scale_inv=sw)
+        dw_args = dict(a=g8, b=x8, fmt_a=E5M2, fmt_b=E4M3, layout=TN, m=n_out, n=n_in, k=t,
+                       a_scale_inv=state.ring_g, b_scale_inv=sx)
+        if ctx.needs_input_grad[0] and ctx.needs_input_grad[1]:
+            dx, dw = fp8_mm_pair(dx_args, dw_args)           # one launch for both
+            dx, dw = dx.view(ctx.x_shape), dw.view(n_out, n_in)
+        elif ctx.needs_input_grad[0]:
+            dx = fp8_mm(**dx_args).view(ctx.x_shape)
+        elif ctx.needs_input_grad[1]:
+            dw = fp8_mm(**dw_args).view(n_out, n_in)
         if ctx.has_bias and ctx.needs_input_grad[2]:
             db = fp8_bias_grad(g2, t, n_out, workspace=state.bias_workspace(t, n_out, g2.device))
         return dx, dw, db, None

@@ -267,6 +267,19 @@ int fp8_mm_with_tile(const fp8_mm_args* args, int tile, void* stream);
  * max_workgroups < 0 or > 2^31-1 is FP8DS_EINVAL. */
 int fp8_mm_with_grid(const fp8_mm_args* args, int tile, int max_workgroups, void* stream);
 
+/* Two independent fp8_mm calls, each exactly as fp8_mm on its own arguments
+ * (its output bits included), issued together: a layer's dX = G.W (NN) and
+ * dW = G^T.X (TN) on the forward's codes (fp8.py history @f4c44ebf,
+ * forward-carries-scale entry: the backward's two GEMMs).  When `first` is
+ * NN and `second` is TN with the same fmt_a and fmt_b, both run in one launch
+ * whose workgroups are split between them, so small GEMMs that each leave
+ * most of the chip idle share it; any other pair runs as two launches in
+ * order.  Each argument set is validated as fp8_mm validates it, and neither
+ * output may overlap the other problem's operands, bias or output
+ * (FP8DS_EINVAL); nothing is launched on an error.  An empty problem (m or n
+ * zero) is skipped. */
+int fp8_mm_pair(const fp8_mm_args* first, const fp8_mm_args* second, void* stream);
+
 /* Message of the last non-zero status returned on the calling thread. */
 const char* fp8_last_error(void);
 

@@ -156,3 +156,24 @@ def test_batch_quantize_validates_before_launch(L):
     assert L.fp8_quantize_batch(jobs((1 << 21 | 8, 4096, 1 << 13, 1 << 25, None)), 1, 0, 0, None) == -2
     empty = (None, 0, 1 << 14, None, None)
     assert L.fp8_quantize_batch(jobs(empty, empty[:2] + (1 << 15,) + empty[3:]), 2, 0, 0, None) == 0   # nothing to do
+
+
+def test_mm_pair_validates_before_launch(L):
+    def args(a, b, c, layout=1, m=16, n=16, k=16):
+        x = ds._MmArgs()
+        x.a, x.b, x.c, x.layout, x.m, x.n, x.k = a, b, c, layout, m, n, k
+        x.a_scale_inv, x.b_scale_inv = 1 << 30, 1 << 30
+        x.lda = x.ldb = x.ldc = 16
+        return x
+    first = args(1 << 20, 1 << 21, 1 << 22)
+    second = args(1 << 23, 1 << 24, 1 << 25, layout=2)
+    assert L.fp8_mm_pair(None, ctypes.byref(second), None) == -1
+    bad = args(1 << 23, 1 << 24, 1 << 25, layout=7)
+    assert L.fp8_mm_pair(ctypes.byref(first), ctypes.byref(bad), None) == -1
+    onto_a = args(1 << 23, 1 << 24, 1 << 20, layout=2)          # second writes first's A
+    assert L.fp8_mm_pair(ctypes.byref(first), ctypes.byref(onto_a), None) == -1
+    assert b"overlaps" in L.fp8_last_error()
+    same_c = args(1 << 23, 1 << 24, (1 << 22) + 256, layout=2)   # outputs overlap
+    assert L.fp8_mm_pair(ctypes.byref(first), ctypes.byref(same_c), None) == -1
+    e0, e1 = args(None, None, 1 << 22, m=0), args(None, None, 1 << 25, n=0, layout=2)
+    assert L.fp8_mm_pair(ctypes.byref(e0), ctypes.byref(e1), None) == 0       # both empty: nothing to do
