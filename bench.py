@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-rows", type=int, default=256, help="output rows of the oracle sample")
     ap.add_argument("--no-widened", action="store_true", help="skip the widened-path kernel timings")
+    ap.add_argument("--no-linear-step", action="store_true", help="skip the 12-layer linear step")
     return ap.parse_args()
 
 
@@ -168,7 +169,9 @@ def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
     """Forward + backward of the linear layers of a 12-layer, dim-1024 model on
     2048 tokens (per layer QKV 1024->3072, O 1024->1024, MLP up 1024->4096 and
     down 4096->1024, no bias): the library's FP8 layer against torch's bf16
-    linear, each linear with its own synthetic input and output gradient."""
+    linear, each linear with its own synthetic input and output gradient.
+    Every step starts with the gradients unset, as after an optimizer's
+    zero_grad(set_to_none=True), so backward writes them without an add."""
     import torch
     from delayed_scaling_amd.linear import Fp8Linear
     shapes = [(dim, 3 * dim), (dim, dim), (dim, 4 * dim), (4 * dim, dim)] * layers
@@ -180,6 +183,8 @@ def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
 
     def run(mods):
         for m, x, g in zip(mods, xs, gs):
+            x.grad = None                      # as an optimizer's zero_grad(set_to_none=True)
+            m.weight.grad = None
             m(x).backward(g)
 
     def timed(fn):
@@ -210,7 +215,7 @@ def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
         res[name] = timed(graph.replay)
     flops = 6.0 * tokens * sum(i * o for i, o in shapes)
     return {"workload": f"{layers} layers x 4 linears (dim {dim}, {tokens} tokens), forward + backward, no bias, "
-                        "each step captured in a HIP graph",
+                        "gradients set to None before each step, each step captured in a HIP graph",
             "fp8_ms_per_step": round(res["fp8"], 3), "bf16_ms_per_step": round(res["bf16"], 3),
             "speedup_vs_bf16": round(res["bf16"] / res["fp8"], 3),
             "fp8_tflops": round(flops / (res["fp8"] * 1e-3) / 1e12, 1),
@@ -324,7 +329,8 @@ def main():
         del A, B, A8, B8, C, cal_src, cal_dst
         torch.cuda.empty_cache()
         out["widened"] = measure_widened(ds, n, stream)
-        out["widened"]["linear_step_12_layers"] = measure_linear_step(stream)
+        if not args.no_linear_step:
+            out["widened"]["linear_step_12_layers"] = measure_linear_step(stream)
         qsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip")
         gsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip")
         for name, entry in out["widened"].items():
