@@ -134,3 +134,18 @@ def test_long_history_windows(hist_len):
             assert_ring_equal(ring.read(), ref, t)
     torch.cuda.synchronize()
     assert_ring_equal(ring.read(), ref, "end")
+
+
+def test_batch_at_the_bench_step_configuration():
+    """A and B of the headline workload (8192 x 8192 bf16 each, history 16) in
+    one batched launch, as the benchmark step issues them: two steps, codes,
+    rings and applied 1/scale outputs bit-exact against the oracle."""
+    ds = require_gpu()
+    from synth import seed_for
+    a = bf16_normal((8192, 8192), seed_for(3, 0, "A"))
+    b = bf16_normal((8192, 8192), seed_for(3, 0, "B"))
+    rings = [ds.ScaleRing(16, oracle.E4M3), ds.ScaleRing(16, oracle.E4M3)]
+    refs = [oracle.ring_init(16, oracle.E4M3), oracle.ring_init(16, oracle.E4M3)]
+    for step in range(2):
+        say(f"bench-configuration batch step {step}")
+        refs = check_batch(ds, [a.reshape(-1), b.reshape(-1)], oracle.IN_BF16, oracle.E4M3, rings, refs)
