@@ -90,7 +90,9 @@ def fp8_linear(x, weight, bias, state):
 
 
 class Fp8Linear(torch.nn.Module):
-    """Drop-in linear layer (bf16 parameters) computing in FP8."""
+    """Drop-in linear layer (bf16 parameters) computing in FP8.  in_features
+    and out_features must be multiples of 16 (the GEMM's 16-byte row
+    alignment); any number of tokens."""
 
     def __init__(self, in_features, out_features, bias=True, hist_len=16, device="cuda"):
         super().__init__()
