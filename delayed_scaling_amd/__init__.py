@@ -119,8 +119,10 @@ def _check(status):
 
 
 def _stream(stream):
+    """The HIP stream to launch on: the given torch stream, else the current
+    stream of the current device (read without building a Stream object)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
     return ctypes.c_void_p(stream.cuda_stream)
 
 

@@ -110,3 +110,23 @@ def test_results_do_not_depend_on_the_tile():
         torch.cuda.synchronize()
         for t in range(1, 7):
             assert same_bits(outs[0], outs[t]), (layout, t)
+
+
+def test_pair_of_batched_problems():
+    """Batched NN and TN problems (strided batches, and a weight broadcast with
+    batch stride 0 in the first) in one pair launch equal their single calls."""
+    ds = require_gpu()
+    batch, t, n_in, n_out = 3, 272, 160, 208
+    rng_codes = lambda shape, seed, fmt: to_dev_u8(random_codes(shape, seed, FINITE[fmt]))
+    g8 = rng_codes((batch, t, n_out), 90, 1)
+    w8 = rng_codes((n_out, n_in), 91, 0)                      # shared by every batch entry
+    x8 = rng_codes((batch, t, n_in), 92, 0)
+    s = [scale_tensor(v) for v in (0.013, 0.029, 0.041)]
+    dx = dict(a=g8, b=w8, fmt_a=1, fmt_b=0, layout=oracle.NN, m=t, n=n_in, k=n_out, a_scale_inv=s[0],
+              b_scale_inv=s[1], batch=batch, stride_a=t * n_out, stride_b=0, stride_c=t * n_in)
+    dw = dict(a=g8, b=x8, fmt_a=1, fmt_b=0, layout=oracle.TN, m=n_out, n=n_in, k=t, a_scale_inv=s[0],
+              b_scale_inv=s[2], batch=batch, stride_a=t * n_out, stride_b=t * n_in, stride_c=n_out * n_in)
+    o0, o1 = ds.fp8_mm_pair(dx, dw)
+    s0, s1 = ds.fp8_mm(**dx), ds.fp8_mm(**dw)
+    torch.cuda.synchronize()
+    assert same_bits(o0, s0) and same_bits(o1, s1)
