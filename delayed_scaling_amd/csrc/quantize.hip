@@ -548,9 +548,11 @@ __global__ __launch_bounds__(kQBlock) void amax_kernel(const v4u* __restrict__ x
 // codes dequantized as dec(code) * s_inv.  A block takes 64 columns and a
 // slice of the rows; thread t sums columns 8*(t%8) .. +7 over rows t/8,
 // t/8 + 32, ... of its slice, the 32 row lanes are added in a fixed order in
-// LDS, and the slice's 64 sums go to the workspace.  The last block of a
-// column strip (a ticket per strip, as in the ring's completion tree) adds
-// the slices in order, so the result does not depend on timing.  Partial sums
+// LDS, and the slice's 64 sums go to the workspace.  Consecutive blocks take
+// consecutive strips of one slice, so the blocks running together read whole
+// rows.  The last block of a column strip (a ticket per strip, as in the
+// ring's completion tree) adds the slices in order, its loads of them issued
+// sixteen at a time, so the result does not depend on timing.  Partial sums
 // travel as device-scope atomic stores and loads, so they are seen across
 // XCDs without writing back any cache.  The last block clears what it read
 // and its ticket: the whole workspace is zero again after every call, so one
@@ -594,7 +596,7 @@ __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __res
   constexpr int kElem = GT == kGF32 ? 4 : (GT == kGBf16 || GT == kGF16) ? 2 : 1;
   __shared__ float sums[32][kGradCols + 1];
   __shared__ int s_last;
-  const int strip = blockIdx.x / slices, slice = blockIdx.x % slices;
+  const int strips = (int)gridDim.x / slices, strip = blockIdx.x % strips, slice = blockIdx.x / strips;
   const int c0 = strip * kGradCols;
   const int cg = threadIdx.x & 7, rl = threadIdx.x >> 3;   // 8-column group, row lane
   const int col = c0 + 8 * cg;
@@ -630,12 +632,23 @@ __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __res
   __syncthreads();
   if (!s_last) return;
   if (threadIdx.x < kGradCols && c0 + (int)threadIdx.x < cols) {
+    // The slices' sums in slice order; each group of 16 loads goes out
+    // together, and every slot is cleared once all are read.
     float s = 0.f;
-    for (int j = 0; j < slices; ++j) {
-      float* pp = partial + (int64_t)j * cols + c0 + threadIdx.x;
-      s += __hip_atomic_load(pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pp, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    float* const p0 = partial + c0 + threadIdx.x;
+    for (int j0 = 0; j0 < slices; j0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = j0 + u < slices ? __hip_atomic_load(p0 + (int64_t)(j0 + u) * cols, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (j0 + u < slices) s += v[u];
     }
+    for (int j = 0; j < slices; ++j)
+      __hip_atomic_store(p0 + (int64_t)j * cols, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (out_f32) static_cast<float*>(out)[c0 + threadIdx.x] = s;
     else static_cast<uint16_t*>(out)[c0 + threadIdx.x] = __builtin_bit_cast(uint16_t, (__bf16)s);
   }
