@@ -70,7 +70,7 @@ enum {
   FP8DS_OK = 0,
   FP8DS_EINVAL = -1,      /* null pointer, bad enum, negative or oversized dimension  */
   FP8DS_EALIGN = -2,      /* base pointer or leading dimension not 16-byte aligned    */
-  FP8DS_EUNSUPPORTED = -3,/* valid request this build does not implement              */
+  FP8DS_EUNSUPPORTED = -3,/* valid request the library does not implement             */
   FP8DS_ELAUNCH = -4      /* the HIP runtime rejected the kernel launch               */
 };
 

@@ -14,7 +14,7 @@ What the pages fix:
     dequantized before the sum, and gradients are bf16 (fp8.py history
     @f4c44ebf, backward column-sum entry and the bf16-gradient entry).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * the transposed output of an R x C input is the C x R row-major matrix of
     the same codes; the dual form returns both; every form folds the tensor's
     amax into the ring once, exactly as the plain quantize does;

@@ -9,7 +9,7 @@ quantized (fp8.py history @4dc5e923, entry that skips the meta allocation on
 the dynamic path; history of `tests`, entry merging the two recipes into one
 dataclass with a dynamic flag).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * scale = fl32(FMAX / amax(x)) when amax is finite and positive and the
     quotient is finite, otherwise 1 (an all-zero, infinite or NaN tensor has
     no usable amax);

@@ -11,7 +11,7 @@ mentioned where the collapsed-scale bug is described (fp8.py history
 below are the OCP 8-bit floating point definitions ("e4m3fn": no infinities,
 one NaN mantissa pattern; "e5m2": IEEE-like with infinities).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * encoding is round-to-nearest, ties to the code with even mantissa, and
     saturating: any magnitude at or above the format maximum, infinity
     included, becomes the largest finite code of that sign;

@@ -15,7 +15,7 @@ What the pages fix (AstrAI commit history of astrai/extension/fp8.py,
   * the GEMM dequantizes with the scale the quantize actually applied, kept
     apart from the newly published one (scale snapshot entry).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * direction: q = cast(x * scale) and next scale = FMAX / window_max;
   * the window reduction is the maximum over all hist slots; unwritten slots
     hold 0 and never win;
