@@ -324,7 +324,7 @@ def main():
                    "m": n, "n": n, "k": n, "hist_len": 16, "input_rotation": rot},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm_kernel 256x256 tile, 8 waves, NT, E4M3 x E4M3",
+                     "traffic": traffic, "kernel": "gemm_kernel 256x256 tile, 4 waves, NT, E4M3 x E4M3",
                      "avg_launch_us": round(g_avg * 1e3, 2), "launch_us": spread(g_ms)},
         "roofline_quantize": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": PEAK_HBM_GBPS,
                               "unit": "GB/s", "frac": round(q_gbps / PEAK_HBM_GBPS, 4),

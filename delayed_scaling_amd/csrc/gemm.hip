@@ -163,9 +163,13 @@ __device__ __forceinline__ int slot_kpos(int slot) {
   }
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations
@@ -199,25 +203,109 @@ __device__ __forceinline__ uint32_t swap_lane_halves(uint32_t x, bool hi) {
   return hi ? r[0] : r[1];
 }
 
+// s_waitcnt immediate that waits until none of this wave's LDS operations is
+// outstanding (vmcnt and expcnt left unconstrained).
+constexpr int lgkmcnt_zero_imm() { return 15 | (3 << 14) | (7 << 4); }
+
+// Columns a wave stages through LDS at a time in the epilogue: 32 rows of
+// them fit the wave's LPS KiB share of a stage buffer, and they divide the
+// wave's WN columns.
+constexpr int staged_cols(int wn, int lps) {
+  int cw = wn;
+  while (cw * 64 > lps * 1024) cw /= 2;
+  return cw;
+}
+
+// Epilogue of one wave for a block inside C with no bias, through LDS.  The
+// wave writes y = bf16(acc * alpha) of 32 rows x CW columns to a staging area
+// (each lane its row's 4-column pieces, as the MFMA left them), reads them
+// back row-contiguous and stores 16 bytes per lane, so every store
+// instruction writes whole rows of CW columns: full 128-byte lines.
+// The staging area is the wave's own share of `buf`, the stage buffer the
+// tile's last stage freed: the 1 KiB pieces t * NW + wave, t < LPS, exactly
+// the pieces the wave's next loads into that buffer refill, so no other wave
+// touches them until those loads are issued.  Staged rows are RB bytes; their
+// 16-byte chunks are XOR-swizzled by row so the row-contiguous reads are free
+// of bank conflicts.  LDS operations of one wave run in order, so the reads
+// see the writes and later writes wait for earlier reads.
+template <int BM, int BN, int TM, int TN, int NW, int LPS>
+__device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&acc)[TN][TM], int m0, int n0,
+                                               uint16_t* cb, int lane, int wave, float alpha, lds_char_t* buf) {
+  constexpr uint32_t CW = staged_cols(TN * 32, LPS);
+  constexpr uint32_t RB = 2 * CW, CH = RB / 16, RPP = 1024 / RB, RPI = 64 / CH, NR = 32 / RPI;
+  static_assert(CW >= 32 && (TN * 32) % CW == 0 && 32 * RB <= LPS * 1024, "staging area");
+  uint8_t* base = reinterpret_cast<uint8_t*>(cb + (int64_t)m0 * p.ldc + n0);
+  const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
+  // The per-lane staging addresses are cheap: compute them here, not once
+  // for the whole kernel, where they would hold registers through the K loop.
+  uint32_t ul = (uint32_t)lane;
+  asm volatile("" : "+v"(ul));
+  const uint32_t sbase = lds_address(buf) + (uint32_t)wave * 1024u;
+  auto row_at = [&](uint32_t r) __attribute__((always_inline)) {
+    return sbase + (r / RPP) * (NW * 1024u) + (r % RPP) * RB;
+  };
+  // Write phase: lane l holds MFMA row l % 32, column half l / 32.
+  const uint32_t wr = ul & 31u, wsw = wr % CH, waddr = row_at(wr) + 8u * (ul >> 5);
+  // Read phase: lane l reads chunk l % CH of row l / CH (+ RPI per read).
+  const uint32_t rr = ul / CH, rc = ul % CH;
+  const uint32_t goff = rr * ldc2 + rc * 16u;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+#pragma unroll
+    for (uint32_t cc = 0; cc < TN * 32 / CW; ++cc) {
+#pragma unroll
+      for (uint32_t il = 0; il < CW / 32; ++il) {
+        const v16f& a = acc[cc * (CW / 32) + il][j];
+#pragma unroll
+        for (uint32_t rq = 0; rq < 4; ++rq) {
+          // fma with +0 as the bias: a zero product rounds to +0, as with a bias.
+          const uint32_t lo = pack_bf16x2(__builtin_fmaf(a[4 * rq + 0], alpha, 0.f), __builtin_fmaf(a[4 * rq + 1], alpha, 0.f));
+          const uint32_t hi = pack_bf16x2(__builtin_fmaf(a[4 * rq + 2], alpha, 0.f), __builtin_fmaf(a[4 * rq + 3], alpha, 0.f));
+          const uint32_t addr = waddr + (((4u * il + rq) ^ wsw) << 4);
+          *(lds_v2i_t*)((lds_char_t*)(uintptr_t)addr) = v2i{(int)lo, (int)hi};
+        }
+      }
+      v4i val[NR];
+#pragma unroll
+      for (uint32_t q = 0; q < NR; ++q) {
+        const uint32_t r = q * RPI + rr;
+        val[q] = *(const lds_v4i_t*)((lds_char_t*)(uintptr_t)(row_at(r) + ((rc ^ (r % CH)) << 4)));
+      }
+      uint8_t* band = base + (uint32_t)j * 32u * ldc2 + cc * CW * 2u;
+#pragma unroll
+      for (uint32_t q = 0; q < NR; ++q)
+        *reinterpret_cast<v4i*>(band + goff + q * RPI * ldc2) = val[q];
+      // One row band at a time: interleaving the bands holds more registers
+      // than the K loop leaves free.
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // Epilogue of one wave for output tile v: y = acc * alpha + bias[n] with one
 // bf16 rounding, alpha = sa_inv * sb_inv.  The wave's C block starts at row
 // r0 and column c0 of the tile; lane l holds rows +l%32 and four consecutive
 // columns per 8-column group of each 32 x 32 MFMA tile.
 //
-// A block inside C with no bias takes the fast path: two column groups are
-// combined by swapping half of them between the lane halves, so every lane
-// stores 8 consecutive columns (16 bytes) and each store instruction writes
-// 32 rows x 32 contiguous bytes, with offsets relative to the block's scalar
-// base.  It issues no loads, so nothing waits on the loads of the next tile
-// that are already in flight.  Edge blocks and bias go through the guarded
-// path, whose bias loads make the wave wait for those loads.
-template <int BM, int BN, int TM, int TN>
+// A block inside C with no bias stores through LDS (store_c_staged) when the
+// caller hands over a free stage buffer; without one (a launch with K = 0)
+// it takes the register path: two column groups are combined by swapping half
+// of them between the lane halves, so every lane stores 8 consecutive columns
+// (16 bytes) and each store instruction writes 32 rows x 32 contiguous bytes.
+// Neither issues loads, so nothing waits on the loads of the next tile that
+// are already in flight.  Edge blocks and bias go through the guarded path,
+// whose bias loads make the wave wait for those loads.
+template <int BM, int BN, int TM, int TN, int NW, int LPS>
 __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
-                                             int lane, float alpha) {
+                                             int lane, int wave, float alpha, lds_char_t* stage_buf) {
   int bt, tmi, tni;
   map_tile(p, v, bt, tmi, tni);
   const int m0 = tmi * BM + r0, n0 = tni * BN + c0;
   uint16_t* cb = p.c + bt * p.stride_c;
+  if (stage_buf && p.bias_kind == 0 && p.ldc_small && m0 + TM * 32 <= p.m && n0 + TN * 32 <= p.n) {
+    store_c_staged<BM, BN, TM, TN, NW, LPS>(p, acc, m0, n0, cb, lane, wave, alpha, stage_buf);
+    return;
+  }
   // (Blocks of more than 8 MFMA tiles keep their accumulators in AGPRs; for
   // them the fast path's extra registers cost more than it saves.)
   if (TM * TN <= 8 && p.bias_kind == 0 && p.ldc_small && m0 + TM * 32 <= p.m && n0 + TN * 32 <= p.n) {
@@ -503,7 +591,8 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   zero_acc(acc);
   if (kt_total == 0) {          // K = 0: every output is bf16(bias) or zero
     const float alpha = make_alpha();
-    for (int it = 0; it < my_tiles; ++it) store_c_tile<BM, BN>(p, acc, wg + it * G, r0, c0, lane, alpha);
+    for (int it = 0; it < my_tiles; ++it)
+      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, nullptr);
     return;
   }
 
@@ -526,11 +615,13 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
   // One stage s: make stage s+1 visible, then issue stage s's MFMAs one by
-  // one, each followed by its share of the global loads of stage s+kStages
-  // (into the buffer stage s freed) and, when READ, of the LDS reads of stage
+  // one, each followed, when READ, by its share of the global loads of stage
+  // s+kStages (into the buffer stage s freed) and of the LDS reads of stage
   // s+1's fragments into na / nb.  Scheduling barriers keep that interleave:
   // bursts of loads or LDS reads right after the barrier left the matrix cores
   // idle.  The wave runs at raised priority while it issues the MFMA stream.
+  // A tile's last stage (not READ) issues MFMAs only: its buffer stages the
+  // epilogue, and its loads go out after it.
   constexpr int NM = TM * TN, NF = TM + TN;
   auto stage = [&](auto read, int s, int next_k, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM],
                    v8i (&nb)[TN]) __attribute__((always_inline)) {
@@ -546,9 +637,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
     for (int q = 0; q < NM; ++q) {
       const int i = q / TM, j = q % TM;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
-#pragma unroll
-      for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) ld.issue_one(c, l);
       if constexpr (READ) {
+#pragma unroll
+        for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) ld.issue_one(c, l);
 #pragma unroll
         for (int f = q * NF / NM; f < (q + 1) * NF / NM; ++f) {
           if (f < TM) na[f] = load_frag<A_KC, BM>(sa, r0 + f * 32, lane);
@@ -558,7 +649,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    ld.advance(p, my_tiles, kt_total, wave, lane);
+    if constexpr (READ) ld.advance(p, my_tiles, kt_total, wave, lane);
   };
   using Read = std::true_type;
   using NoRead = std::false_type;
@@ -578,10 +669,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   // Each tile starts with its first stage's fragments in set 0 and runs its
   // kt_total - 1 leading stages in pairs that alternate the two fragment
   // sets (one single stage first when their count is odd, its fragments
-  // moved back to set 0).  Its last stage runs the MFMAs and the loads only;
-  // then the tile is stored, the accumulators cleared, and the next stage's
-  // fragments read into set 0, so the epilogue has the registers of both
-  // fragment sets to itself.
+  // moved back to set 0).  Its last stage runs the MFMAs only; then the tile
+  // is stored through that stage's buffer, the stage's loads go out, the
+  // accumulators are cleared and the next stage's fragments read into set 0,
+  // so the epilogue has the registers of both fragment sets to itself.
   for (int it = 0; it < my_tiles; ++it) {
     const int s0 = it * kt_total;
     int kt = 0;
@@ -598,7 +689,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
       stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
     }
     stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
-    store_c_tile<BM, BN>(p, acc, wg + it * G, r0, c0, lane, alpha);
+    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, buf(s0 + kt_total - 1));
+    // The staging reads have returned before the loads refill the area.  (The
+    // loads after the last tile fetch nothing; skipping them with an early
+    // exit made the compiler wait for every outstanding load in the K loop.)
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_zero_imm());
+    ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
     zero_acc(acc);
     read_frags<BM, BN, TM, TN, A_KC, B_KC>(buf(s0 + kt_total), r0, c0, lane, fa0, fb0);
   }
@@ -641,10 +737,11 @@ struct TileCfg {
 };
 // Tile family (index = the tile argument of fp8_mm_with_tile).  256x256 with
 // four waves runs one workgroup per CU (4 LDS stages, 128 KiB), each wave a
-// 128x128 block; the eight-wave 256x256 tiles give every SIMD two waves of a
-// 128x64 / 64x128 block; 256x128 / 128x256 run two workgroups per CU (3
-// stages, 72 KiB each); 128x128 and 64x64 serve problems too small to fill
-// the chip.
+// 128x128 block: the large-problem tile without a bias, as it reads the
+// fewest LDS bytes per MFMA; the eight-wave 256x256 tiles give every SIMD two
+// waves of a 128x64 / 64x128 block (large problems with a bias, and the
+// pair); 256x128 / 128x256 run two workgroups per CU (3 stages, 72 KiB each);
+// 128x128 and 64x64 serve problems too small to fill the chip.
 constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
                               {128, 256, 4}, {256, 256, 8}, {256, 256, 8}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -700,7 +797,7 @@ GemmFn kernel_for(int tile, int layout, int fa, int fb) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile choice by grid size, from per-shape timings on 256 CUs:
-//  * the eight-wave 256x256 tile when its grid fills the CUs;
+//  * a 256x256 tile when its grid fills the CUs;
 //  * else 128x128 when its grid fills them, or half-fills them with K >= 2048
 //    (a half-empty chip of 128x128 tiles beats a full one of 64x64 tiles once
 //    the K loop is long enough to amortize their higher per-tile rate);
@@ -710,22 +807,26 @@ int64_t tile_count(const GemmProblem& p, int t) {
 }
 
 // The rule over a launch's total tile count and (shortest) K.
-int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k) {
+int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k, int big) {
   constexpr int64_t kCUs = 256;
-  if (count(ps, 6) >= kCUs) return 6;
+  if (count(ps, big) >= kCUs) return big;
   const int64_t t1 = count(ps, 1);
   if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 1;
   return 2;
 }
 
+// Large launches take the four-wave 256x256 tile when every interior block
+// stores through LDS (no bias); with a bias, whose per-element epilogue one
+// wave per SIMD cannot hide, the eight-wave one.
 int choose_tile(const GemmProblem& p) {
-  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k);
+  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6);
 }
 
-// For a fused pair: the same rule over both problems' tiles and the shorter K.
+// For a fused pair: the same rule over both problems' tiles and the shorter K
+// (the pair kernel has the eight-wave 256x256 tile).
 int choose_pair_tile(const GemmProblem (&pp)[2]) {
   return tile_for([](const GemmProblem* q, int t) { return tile_count(q[0], t) + tile_count(q[1], t); }, pp,
-                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k);
+                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6);
 }
 
 // Workgroups of one kernel that fit on the device at once (CUs x occupancy),
