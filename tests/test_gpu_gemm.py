@@ -104,6 +104,20 @@ def test_workgroups_running_several_tiles(tile, layout):
              grid=8)                                                                        # 2 stages, batches
 
 
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8"])
+@pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
+def test_epilogue_through_lds(tile, layout):
+    """No bias, so every block inside C is stored through LDS: batches, a
+    padded ldc whose padding columns stay untouched, ragged edge blocks beside
+    interior ones, and two workgroups running 4-5 tiles each (the staging area
+    is the freed stage buffer that the next tile's loads refill)."""
+    ds = require_gpu()
+    say(f"gemm {layout} tile={tile} staged epilogue")
+    lay = LAYOUTS[layout]
+    run_case(ds, lay, 1, 0, 520, 528, 192, batch=2, tile=tile, pad_ld=16, seed=40, grid=2)
+    run_case(ds, lay, 0, 0, 512, 512, 64, tile=tile, seed=41, grid=8)                      # interior only, K = 64
+
+
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_small_integer_products_bit_exact(layout):
     ds = require_gpu()
