@@ -216,11 +216,33 @@ constexpr int staged_cols(int wn, int lps) {
   return cw;
 }
 
-// Epilogue of one wave for a block inside C with no bias, through LDS.  The
-// wave writes y = bf16(acc * alpha) of 32 rows x CW columns to a staging area
-// (each lane its row's 4-column pieces, as the MFMA left them), reads them
-// back row-contiguous and stores 16 bytes per lane, so every store
-// instruction writes whole rows of CW columns: full 128-byte lines.
+// Bias of the four consecutive columns n .. n+3, all inside the output, in
+// fp32: bf16 and fp32 as stored, an 8-bit bias as fl32(dec(code) *
+// bias_scale_inv).  n is a multiple of 4, so each kind is one aligned load.
+__device__ __forceinline__ v4f bias4_full(const GemmKArgs& p, int n) {
+  if (p.bias_kind == 1) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.bias) + n);
+    return v4f{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xFFFF0000u)};
+  }
+  if (p.bias_kind == 2) return *reinterpret_cast<const v4f*>(static_cast<const float*>(p.bias) + n);
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.bias) + n);
+  const float bsi = p.bias_scale_inv[0];
+  v4f r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = (int)(w >> (8 * e));
+    r[e] = (p.bias_kind == 3 ? __builtin_amdgcn_cvt_f32_fp8(c, 0) : __builtin_amdgcn_cvt_f32_bf8(c, 0)) * bsi;
+  }
+  return r;
+}
+
+// Epilogue of one wave for a block inside C, through LDS.  The wave writes
+// y = bf16(acc * alpha + bias) of 32 rows x CW columns to a staging area (each
+// lane its row's 4-column pieces, as the MFMA left them), reads them back
+// row-contiguous and stores 16 bytes per lane, so every store instruction
+// writes whole rows of CW columns: full 128-byte lines.  The bias of the CW
+// columns is loaded once for all row bands.
 // The staging area is the wave's own share of `buf`, the stage buffer the
 // tile's last stage freed: the 1 KiB pieces t * NW + wave, t < LPS, exactly
 // the pieces the wave's next loads into that buffer refill, so no other wave
@@ -232,8 +254,7 @@ template <int BM, int BN, int TM, int TN, int NW, int LPS>
 __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&acc)[TN][TM], int m0, int n0,
                                                uint16_t* cb, int lane, int wave, float alpha, lds_char_t* buf) {
   constexpr uint32_t CW = staged_cols(TN * 32, LPS);
-  constexpr uint32_t RB = 2 * CW, CH = RB / 16, RPP = 1024 / RB, RPI = 64 / CH, NR = 32 / RPI;
-  static_assert(CW >= 32 && (TN * 32) % CW == 0 && 32 * RB <= LPS * 1024, "staging area");
+  static_assert(CW >= 32 && (TN * 32) % CW == 0 && 32 * 2 * CW <= LPS * 1024, "staging area");
   uint8_t* base = reinterpret_cast<uint8_t*>(cb + (int64_t)m0 * p.ldc + n0);
   const uint32_t ldc2 = 2u * (uint32_t)p.ldc;
   // The per-lane staging addresses are cheap: compute them here, not once
@@ -241,45 +262,64 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
   uint32_t ul = (uint32_t)lane;
   asm volatile("" : "+v"(ul));
   const uint32_t sbase = lds_address(buf) + (uint32_t)wave * 1024u;
-  auto row_at = [&](uint32_t r) __attribute__((always_inline)) {
-    return sbase + (r / RPP) * (NW * 1024u) + (r % RPP) * RB;
-  };
-  // Write phase: lane l holds MFMA row l % 32, column half l / 32.
-  const uint32_t wr = ul & 31u, wsw = wr % CH, waddr = row_at(wr) + 8u * (ul >> 5);
-  // Read phase: lane l reads chunk l % CH of row l / CH (+ RPI per read).
-  const uint32_t rr = ul / CH, rc = ul % CH;
-  const uint32_t goff = rr * ldc2 + rc * 16u;
+  const uint32_t wr = ul & 31u, wh = ul >> 5;   // write phase: MFMA row l % 32, column half l / 32
+  // With a bias, at most 64 columns per pass, so their bias values (8 x 4 per
+  // lane) fit the registers the K loop leaves free.
+  auto run = [&](auto with_bias) __attribute__((always_inline)) {
+    constexpr bool HB = decltype(with_bias)::value;
+    constexpr uint32_t SC = HB && CW > 64 ? 64 : CW;   // columns per pass
+    constexpr uint32_t RB = 2 * SC, CH = RB / 16, RPP = 1024 / RB, RPI = 64 / CH, NR = 32 / RPI;
+    constexpr uint32_t SG = SC / 32 * 4;                // 4-column groups of a lane per staged row
+    auto row_at = [&](uint32_t r) __attribute__((always_inline)) {
+      return sbase + (r / RPP) * (NW * 1024u) + (r % RPP) * RB;
+    };
+    const uint32_t wsw = wr % CH, waddr = row_at(wr) + 8u * wh;
+    // Read phase: lane l reads chunk l % CH of row l / CH (+ RPI per read).
+    const uint32_t rr = ul / CH, rc = ul % CH;
+    const uint32_t goff = rr * ldc2 + rc * 16u;
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
+    for (uint32_t cc = 0; cc < TN * 32 / SC; ++cc) {
+      // Without a bias, fma with +0: a zero product rounds to +0, as with one.
+      v4f bias[SG];
 #pragma unroll
-    for (uint32_t cc = 0; cc < TN * 32 / CW; ++cc) {
+      for (uint32_t g = 0; g < SG; ++g)
+        bias[g] = HB ? bias4_full(p, n0 + (int)(cc * SC + (g / 4) * 32 + 8 * (g % 4) + 4 * wh)) : v4f{};
 #pragma unroll
-      for (uint32_t il = 0; il < CW / 32; ++il) {
-        const v16f& a = acc[cc * (CW / 32) + il][j];
+      for (int j = 0; j < TM; ++j) {
 #pragma unroll
-        for (uint32_t rq = 0; rq < 4; ++rq) {
-          // fma with +0 as the bias: a zero product rounds to +0, as with a bias.
-          const uint32_t lo = pack_bf16x2(__builtin_fmaf(a[4 * rq + 0], alpha, 0.f), __builtin_fmaf(a[4 * rq + 1], alpha, 0.f));
-          const uint32_t hi = pack_bf16x2(__builtin_fmaf(a[4 * rq + 2], alpha, 0.f), __builtin_fmaf(a[4 * rq + 3], alpha, 0.f));
-          const uint32_t addr = waddr + (((4u * il + rq) ^ wsw) << 4);
+        for (uint32_t g = 0; g < SG; ++g) {
+          const v16f& a = acc[cc * (SC / 32) + g / 4][j];
+          const uint32_t rq = g % 4;
+          const uint32_t lo = pack_bf16x2(__builtin_fmaf(a[4 * rq + 0], alpha, bias[g][0]),
+                                          __builtin_fmaf(a[4 * rq + 1], alpha, bias[g][1]));
+          const uint32_t hi = pack_bf16x2(__builtin_fmaf(a[4 * rq + 2], alpha, bias[g][2]),
+                                          __builtin_fmaf(a[4 * rq + 3], alpha, bias[g][3]));
+          const uint32_t addr = waddr + ((g ^ wsw) << 4);
           *(lds_v2i_t*)((lds_char_t*)(uintptr_t)addr) = v2i{(int)lo, (int)hi};
         }
-      }
-      v4i val[NR];
+        v4i val[NR];
 #pragma unroll
-      for (uint32_t q = 0; q < NR; ++q) {
-        const uint32_t r = q * RPI + rr;
-        val[q] = *(const lds_v4i_t*)((lds_char_t*)(uintptr_t)(row_at(r) + ((rc ^ (r % CH)) << 4)));
-      }
-      uint8_t* band = base + (uint32_t)j * 32u * ldc2 + cc * CW * 2u;
+        for (uint32_t q = 0; q < NR; ++q) {
+          const uint32_t r = q * RPI + rr;
+          val[q] = *(const lds_v4i_t*)((lds_char_t*)(uintptr_t)(row_at(r) + ((rc ^ (r % CH)) << 4)));
+        }
+        uint8_t* band = base + (uint32_t)j * 32u * ldc2 + cc * SC * 2u;
 #pragma unroll
-      for (uint32_t q = 0; q < NR; ++q)
-        *reinterpret_cast<v4i*>(band + goff + q * RPI * ldc2) = val[q];
-      // One row band at a time: interleaving the bands holds more registers
-      // than the K loop leaves free.
-      __builtin_amdgcn_sched_barrier(0);
+        for (uint32_t q = 0; q < NR; ++q)
+          *reinterpret_cast<v4i*>(band + goff + q * RPI * ldc2) = val[q];
+        // One row band at a time: interleaving the bands holds more registers
+        // than the K loop leaves free.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  if constexpr (TM * TN <= 8) {
+    if (p.bias_kind != 0) {
+      run(std::true_type{});
+      return;
     }
   }
+  run(std::false_type{});
 }
 
 // Epilogue of one wave for output tile v: y = acc * alpha + bias[n] with one
@@ -287,14 +327,14 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
 // r0 and column c0 of the tile; lane l holds rows +l%32 and four consecutive
 // columns per 8-column group of each 32 x 32 MFMA tile.
 //
-// A block inside C with no bias stores through LDS (store_c_staged) when the
-// caller hands over a free stage buffer; without one (a launch with K = 0)
-// it takes the register path: two column groups are combined by swapping half
-// of them between the lane halves, so every lane stores 8 consecutive columns
-// (16 bytes) and each store instruction writes 32 rows x 32 contiguous bytes.
-// Neither issues loads, so nothing waits on the loads of the next tile that
-// are already in flight.  Edge blocks and bias go through the guarded path,
-// whose bias loads make the wave wait for those loads.
+// A block inside C stores through LDS (store_c_staged) when the caller hands
+// over a free stage buffer; without one (a launch with K = 0) a block inside
+// C with no bias takes the register path: two column groups are combined by
+// swapping half of them between the lane halves, so every lane stores 8
+// consecutive columns (16 bytes) and each store instruction writes 32 rows x
+// 32 contiguous bytes.  Edge blocks go through the guarded path.  A bias load
+// makes the wave wait for the next tile's loads already in flight (the
+// compiler cannot count those), once per tile.
 template <int BM, int BN, int TM, int TN, int NW, int LPS>
 __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
                                              int lane, int wave, float alpha, lds_char_t* stage_buf) {
@@ -302,7 +342,10 @@ __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&ac
   map_tile(p, v, bt, tmi, tni);
   const int m0 = tmi * BM + r0, n0 = tni * BN + c0;
   uint16_t* cb = p.c + bt * p.stride_c;
-  if (stage_buf && p.bias_kind == 0 && p.ldc_small && m0 + TM * 32 <= p.m && n0 + TN * 32 <= p.n) {
+  // (Blocks of 16 MFMA tiles, one wave per SIMD, stage no bias: its registers
+  // make the compiler spill in the K loop.)
+  if (stage_buf && (TM * TN <= 8 || p.bias_kind == 0) && p.ldc_small && m0 + TM * 32 <= p.m &&
+      n0 + TN * 32 <= p.n) {
     store_c_staged<BM, BN, TM, TN, NW, LPS>(p, acc, m0, n0, cb, lane, wave, alpha, stage_buf);
     return;
   }
@@ -737,10 +780,10 @@ struct TileCfg {
 };
 // Tile family (index = the tile argument of fp8_mm_with_tile).  256x256 with
 // four waves runs one workgroup per CU (4 LDS stages, 128 KiB), each wave a
-// 128x128 block: the large-problem tile without a bias, as it reads the
-// fewest LDS bytes per MFMA; the eight-wave 256x256 tiles give every SIMD two
-// waves of a 128x64 / 64x128 block (large problems with a bias, and the
-// pair); 256x128 / 128x256 run two workgroups per CU (3 stages, 72 KiB each);
+// 128x128 block: the large-problem tile, as it reads the fewest LDS bytes per
+// MFMA; the eight-wave 256x256 tiles give every SIMD two waves of a 128x64 /
+// 64x128 block (the pair kernel's large tile); 256x128 / 128x256 run two
+// workgroups per CU (3 stages, 72 KiB each);
 // 128x128 and 64x64 serve problems too small to fill the chip.
 constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
                               {128, 256, 4}, {256, 256, 8}, {256, 256, 8}};
@@ -815,9 +858,8 @@ int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, i
   return 2;
 }
 
-// Large launches take the four-wave 256x256 tile when every interior block
-// stores through LDS (no bias); with a bias, whose per-element epilogue one
-// wave per SIMD cannot hide, the eight-wave one.
+// Large launches take the four-wave 256x256 tile without a bias and the
+// eight-wave one, which stages its bias epilogue through LDS, with one.
 int choose_tile(const GemmProblem& p) {
   return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6);
 }
