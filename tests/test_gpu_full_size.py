@@ -98,3 +98,26 @@ def test_backward_layouts_at_full_size(layout):
     torch.cuda.synchronize()
     check_mm(ds, y, a.reshape(-1), b.reshape(-1), oracle.E5M2, oracle.E4M3, layout, N, N, N, sa, sb, sample=200,
              what=f"8192^3 layout {layout}")
+
+
+def test_bias_gemm_at_full_size():
+    """8192 x 8192 x 1024 NT with a bf16 bias: the automatic choice (the
+    eight-wave 256x256 tile, bias staged through LDS) on sampled entries, and
+    bit-equal to the four-wave tile's per-element bias path."""
+    ds = require_gpu()
+    m = n = N
+    k = 1024
+    a = random_codes((m, k), 4300, FINITE[oracle.E4M3])
+    b = random_codes((n, k), 4301, FINITE[oracle.E4M3])
+    bias = bf16_normal((n,), 4302)
+    sa, sb = 0.0131, 0.0173
+    say("full-size GEMM with bias")
+    kw = dict(bias=to_dev_bf16(bias))
+    y = ds.fp8_mm(to_dev_u8(a), to_dev_u8(b), oracle.E4M3, oracle.E4M3, oracle.NT, m, n, k, scale_tensor(sa),
+                  scale_tensor(sb), **kw)
+    y0 = ds.fp8_mm(to_dev_u8(a), to_dev_u8(b), oracle.E4M3, oracle.E4M3, oracle.NT, m, n, k, scale_tensor(sa),
+                   scale_tensor(sb), tile=0, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+    check_mm(ds, y, a.reshape(-1), b.reshape(-1), oracle.E4M3, oracle.E4M3, oracle.NT, m, n, k, sa, sb, bias=bias,
+             sample=300, what="8192x8192x1024 NT with bias")
