@@ -237,12 +237,12 @@ __device__ __forceinline__ v4f bias4_full(const GemmKArgs& p, int n) {
   return r;
 }
 
-// Epilogue of one wave for a block inside C, through LDS.  The wave writes
-// y = bf16(acc * alpha + bias) of 32 rows x CW columns to a staging area (each
-// lane its row's 4-column pieces, as the MFMA left them), reads them back
-// row-contiguous and stores 16 bytes per lane, so every store instruction
-// writes whole rows of CW columns: full 128-byte lines.  The bias of the CW
-// columns is loaded once for all row bands.
+// Epilogue of one wave for a block inside C, through LDS.  Per pass of SC
+// columns (CW, or 64 with a bias) and per band of 32 rows, the wave writes
+// y = bf16(acc * alpha + bias) to a staging area (each lane its row's 4-column
+// pieces, as the MFMA left them), reads them back row-contiguous and stores 16
+// bytes per lane, so every store instruction writes whole rows of SC columns:
+// full 128-byte lines.  A pass loads its columns' bias once for all bands.
 // The staging area is the wave's own share of `buf`, the stage buffer the
 // tile's last stage freed: the 1 KiB pieces t * NW + wave, t < LPS, exactly
 // the pieces the wave's next loads into that buffer refill, so no other wave
@@ -328,7 +328,8 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
 // columns per 8-column group of each 32 x 32 MFMA tile.
 //
 // A block inside C stores through LDS (store_c_staged) when the caller hands
-// over a free stage buffer; without one (a launch with K = 0) a block inside
+// over a free stage buffer (with a bias, only blocks of at most 8 MFMA tiles);
+// without one (a launch with K = 0) a block inside
 // C with no bias takes the register path: two column groups are combined by
 // swapping half of them between the lane halves, so every lane stores 8
 // consecutive columns (16 bytes) and each store instruction writes 32 rows x
