@@ -130,12 +130,49 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name, dtypes, nbytes, device=True):
+    """Check a tensor before its address goes to a kernel: one of `dtypes`,
+    contiguous, holding at least the `nbytes` bytes the call touches from its
+    first element, and (unless device=False, when the caller checks that for
+    all its tensors afterwards with _on_device) in GPU memory.  The C side
+    checks sizes against each other but cannot see allocations, so a short
+    buffer is caught here, before any launch.  (Attribute reads only: this
+    runs on every call.)"""
+    if not isinstance(t, torch.Tensor):
+        raise Fp8dsError(f"{name} must be a torch tensor" if t is not None else f"{name} is required")
+    if t.dtype not in dtypes:
+        raise Fp8dsError(f"{name} has dtype {t.dtype}; expected {' or '.join(str(d) for d in dtypes)}")
+    if not t.is_contiguous():
+        raise Fp8dsError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise Fp8dsError(f"{name} holds {have} bytes; the call touches {nbytes}")
+    if device:
+        _on_device((name, t))
+    return t
+
+
+def _on_device(*named):
+    """Every given (name, tensor) pair holds GPU memory (None entries skipped)."""
+    for name, t in named:
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise Fp8dsError(f"{name} must be a CUDA (HIP) device tensor")
+
+
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+
+
 def scale_ring_bytes(hist_len):
     return int(lib().fp8_scale_ring_bytes(int(hist_len)))
 
 
 def scale_ring_init(ring, hist_len, fmt, init_scale=1.0, stream=None):
     """Initialise `ring` (a uint8 device tensor of scale_ring_bytes bytes)."""
+    n = scale_ring_bytes(hist_len)
+    if n == 0:
+        raise Fp8dsError(f"hist_len {hist_len} outside [1, 1024]")
+    _need(ring, "ring", _U8, n)
     _check(lib().scale_ring_init(_ptr(ring), int(hist_len), int(fmt), float(init_scale), _stream(stream)))
 
 
@@ -182,15 +219,25 @@ def _in_type(x):
 
 
 def _ring_buf(ring):
-    return ring.buf if isinstance(ring, ScaleRing) else ring
+    """The ring's device buffer; a raw tensor must hold at least a ring of
+    history length 1 (its own length is in its device header)."""
+    buf = ring.buf if isinstance(ring, ScaleRing) else ring
+    return _need(buf, "ring", _U8, scale_ring_bytes(1))
+
+
+def _codes_out(out, numel, device, name="out"):
+    """A uint8 output of numel codes: the given tensor, checked, or a new one."""
+    if out is None:
+        return torch.empty(numel, dtype=torch.uint8, device=device)
+    return _need(out, name, _U8, numel)
 
 
 def fp8_quantize(x, fmt, ring, out=None, stream=None, max_blocks=None):
     """Quantize x (bf16, fp16 or fp32) with the ring's scale into uint8 codes;
     advances the ring."""
     in_type = _in_type(x)
-    if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else \
+        _codes_out(out, x.numel(), x.device)
     rbuf = _ring_buf(ring)
     if max_blocks is not None:
         if in_type != IN_BF16:
@@ -218,7 +265,16 @@ def fp8_quantize_batch(xs, fmt, rings, outs=None, scale_inv_outs=None, stream=No
         raise Fp8dsError("fp8_quantize_batch: all tensors must share one dtype")
     if outs is None:
         outs = [torch.empty(x.shape, dtype=torch.uint8, device=x.device) for x in xs]
+    if len(outs) != n:
+        raise Fp8dsError("fp8_quantize_batch needs one output per tensor")
+    for i in range(n):
+        _codes_out(outs[i], xs[i].numel(), xs[i].device, f"outs[{i}]")
     sio = scale_inv_outs if scale_inv_outs is not None else [None] * n
+    if len(sio) != n:
+        raise Fp8dsError("fp8_quantize_batch needs one scale_inv_outs entry (or None) per tensor")
+    for i in range(n):
+        if sio[i] is not None:
+            _need(sio[i], f"scale_inv_outs[{i}]", _F32, 4)
     jobs = (_QuantJob * n)()
     for i in range(n):
         jobs[i] = _QuantJob(xs[i].data_ptr(), xs[i].numel(), _ring_buf(rings[i]).data_ptr(), outs[i].data_ptr(),
@@ -234,10 +290,14 @@ def fp8_quantize_2d(x, fmt, ring, layout, out=None, out_t=None, stream=None):
     if x.dim() != 2:
         raise Fp8dsError("x must be 2-D")
     rows, cols = x.shape
-    if layout in (ROWWISE, DUAL) and out is None:
-        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
-    if layout in (TRANSPOSED, DUAL) and out_t is None:
-        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if layout not in (ROWWISE, TRANSPOSED, DUAL):
+        raise Fp8dsError(f"layout {layout} is not ROWWISE, TRANSPOSED or DUAL")
+    if layout in (ROWWISE, DUAL):
+        out = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if out is None else \
+            _need(out, "out", _U8, rows * cols)
+    if layout in (TRANSPOSED, DUAL):
+        out_t = torch.empty((cols, rows), dtype=torch.uint8, device=x.device) if out_t is None else \
+            _need(out_t, "out_t", _U8, rows * cols)
     _check(lib().fp8_quantize_2d(_ptr(x), rows, cols, in_type, int(fmt), int(layout), _ptr(_ring_buf(ring)),
                                  _ptr(out) if layout != TRANSPOSED else None,
                                  _ptr(out_t) if layout != ROWWISE else None, _stream(stream)))
@@ -248,8 +308,8 @@ def fp8_quantize_dynamic(x, fmt, ring, out=None, stream=None):
     """Dynamic scaling: quantize x with FMAX / amax(x); ring must have hist_len 1
     and afterwards holds scale_inv_used for the GEMM."""
     in_type = _in_type(x)
-    if out is None:
-        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else \
+        _codes_out(out, x.numel(), x.device)
     _check(lib().fp8_quantize_dynamic(_ptr(x), x.numel(), in_type, int(fmt), _ptr(_ring_buf(ring)), _ptr(out),
                                       _stream(stream)))
     return out
@@ -282,11 +342,19 @@ def fp8_bias_grad(g, rows=None, cols=None, fmt=None, g_scale_inv=None, out_f32=F
         g_type = {torch.bfloat16: G_BF16, torch.float16: G_F16, torch.float32: G_F32}.get(g.dtype)
         if g_type is None:
             raise Fp8dsError("g must be bf16, fp16, fp32 or uint8 codes")
+    esize = {G_E4M3: 1, G_E5M2: 1, G_F32: 4}.get(g_type, 2)
+    _need(g, "g", (g.dtype,), int(rows) * int(cols) * esize, device=False)
+    out_dtype = torch.float32 if out_f32 else torch.bfloat16
     if out is None:
-        out = torch.empty(int(cols), dtype=torch.float32 if out_f32 else torch.bfloat16, device=g.device)
+        out = torch.empty(int(cols), dtype=out_dtype, device=g.device)
+    _need(out, "out", (out_dtype,), int(cols) * (4 if out_f32 else 2), device=False)
+    if g_type in (G_E4M3, G_E5M2) and isinstance(g_scale_inv, torch.Tensor):
+        _need(g_scale_inv, "g_scale_inv", _F32, 4, device=False)
     if workspace is None:
         workspace = BiasGradWorkspace(rows, cols, g.device)
     wbuf = workspace.buf if isinstance(workspace, BiasGradWorkspace) else workspace
+    _need(wbuf, "workspace", _U8, bias_grad_workspace_bytes(rows, cols), device=False)
+    _on_device(("g", g), ("out", out), ("g_scale_inv", g_scale_inv), ("workspace", wbuf))
     _check(lib().fp8_bias_grad(_ptr(g), int(rows), int(cols), g_type, _addr(g_scale_inv), int(bool(out_f32)),
                                _ptr(out), _ptr(wbuf), _stream(stream)))
     return out
@@ -317,8 +385,18 @@ def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias
     stride_b = b_rows * ldb if stride_b is None else stride_b
     stride_c = m * ldc if stride_c is None else stride_c
     dev = a.device if a is not None else b.device
+    nb = max(int(batch), 1)
     if out is None:
-        out = torch.empty(batch * stride_c if batch > 1 else m * ldc, dtype=torch.bfloat16, device=dev)
+        out = torch.empty(nb * stride_c if nb > 1 else m * ldc, dtype=torch.bfloat16, device=dev)
+    if m > 0 and n > 0:
+        # The extents the kernel touches, as the C side computes them: one
+        # batch entry of a stored [rows][cols] view spans (rows-1)*ld + cols
+        # elements; stride 0 broadcasts one entry.
+        ext = lambda rows, cols, ld: (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
+        if k > 0:
+            _need(a, "a", _U8, (nb - 1) * stride_a + ext(a_rows, a_cols, lda), device=False)
+            _need(b, "b", _U8, (nb - 1) * stride_b + ext(b_rows, b_cols, ldb), device=False)
+        _need(out, "out", (torch.bfloat16,), 2 * ((nb - 1) * stride_c + ext(m, n, ldc)), device=False)
     bias_kind = BIAS_NONE
     if bias is not None:
         if bias.dtype == torch.uint8:
@@ -329,6 +407,12 @@ def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias
             bias_kind = {torch.bfloat16: BIAS_BF16, torch.float32: BIAS_F32}.get(bias.dtype)
         if bias_kind is None:
             raise Fp8dsError("bias must be bf16, fp32 or uint8 codes")
+        _need(bias, "bias", (bias.dtype,), n * bias.element_size(), device=False)
+    for nm, sc in (("a_scale_inv", a_scale_inv), ("b_scale_inv", b_scale_inv), ("bias_scale_inv", bias_scale_inv)):
+        if isinstance(sc, torch.Tensor):
+            _need(sc, nm, _F32, 4, device=False)
+    _on_device(("a", a), ("b", b), ("out", out), ("bias", bias), ("a_scale_inv", a_scale_inv),
+               ("b_scale_inv", b_scale_inv), ("bias_scale_inv", bias_scale_inv))
     args = _MmArgs(_addr(a), _addr(b), _addr(out), int(fmt_a), int(fmt_b), int(layout), bias_kind,
                    int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
                    int(stride_a), int(stride_b), int(stride_c),

@@ -33,7 +33,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool valid_fmt(int f) { return f == FP8DS_E4M3 || f == FP8DS_E5M2; }
 bool valid_in(int t) { return t == FP8DS_IN_BF16 || t == FP8DS_IN_F16 || t == FP8DS_IN_F32; }
 int64_t in_size(int t) { return t == FP8DS_IN_F32 ? 4 : 2; }
+// True when the byte ranges [a, a + a_bytes) and [b, b + b_bytes) share a
+// byte; an empty range overlaps nothing.
 bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  if (a_bytes <= 0 || b_bytes <= 0 || !a || !b) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
 }
@@ -69,6 +72,20 @@ int64_t view_extent(int64_t rows, int64_t cols, int64_t ld) {
 
 namespace fp8ds {
 namespace {
+
+// Bytes from c that a problem's output spans, and likewise its operands
+// (stride 0 broadcasts span one entry) and its bias.
+int64_t mm_c_bytes(const GemmProblem& p) {
+  return ((int64_t)(p.batch - 1) * p.stride_c + (int64_t)(p.m - 1) * p.ldc + p.n) * 2;
+}
+int64_t mm_operand_bytes(uint32_t extent, const GemmProblem& p, bool is_b = false) {
+  if (p.k == 0) return 0;
+  return (int64_t)(p.batch - 1) * (is_b ? p.stride_b : p.stride_a) + extent;
+}
+int64_t mm_bias_bytes(const GemmProblem& p) {
+  const int64_t e = p.bias_kind == FP8DS_BIAS_F32 ? 4 : p.bias_kind == FP8DS_BIAS_BF16 ? 2 : 1;
+  return p.n * e;
+}
 
 int check_mm(const fp8_mm_args* a, GemmProblem* out, bool* empty) {
   if (!a) return set_error(FP8DS_EINVAL, "fp8_mm: args is NULL");
@@ -129,22 +146,14 @@ int check_mm(const fp8_mm_args* a, GemmProblem* out, bool* empty) {
   p.b_scale_inv = a->b_scale_inv;
   p.bias = a->bias;
   p.bias_scale_inv = a->bias_scale_inv;
+  // The output is written while the operands and the bias are still read.
+  const int64_t c_bytes = mm_c_bytes(p);
+  if (overlaps(p.c, c_bytes, p.a, mm_operand_bytes(p.extent_a, p)) ||
+      overlaps(p.c, c_bytes, p.b, mm_operand_bytes(p.extent_b, p, true)) ||
+      (p.bias_kind != FP8DS_BIAS_NONE && overlaps(p.c, c_bytes, p.bias, mm_bias_bytes(p))))
+    return set_error(FP8DS_EINVAL, "fp8_mm: c overlaps a, b or bias");
   *out = p;
   return FP8DS_OK;
-}
-
-// Bytes from c that a problem's output spans, and likewise its operands
-// (stride 0 broadcasts span one entry) and its bias.
-int64_t mm_c_bytes(const GemmProblem& p) {
-  return ((int64_t)(p.batch - 1) * p.stride_c + (int64_t)(p.m - 1) * p.ldc + p.n) * 2;
-}
-int64_t mm_operand_bytes(uint32_t extent, const GemmProblem& p, bool is_b = false) {
-  if (p.k == 0) return 0;
-  return (int64_t)(p.batch - 1) * (is_b ? p.stride_b : p.stride_a) + extent;
-}
-int64_t mm_bias_bytes(const GemmProblem& p) {
-  const int64_t e = p.bias_kind == FP8DS_BIAS_F32 ? 4 : p.bias_kind == FP8DS_BIAS_BF16 ? 2 : 1;
-  return p.n * e;
 }
 
 }  // namespace

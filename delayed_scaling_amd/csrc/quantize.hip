@@ -55,7 +55,12 @@ struct In<kInF16> {
   static constexpr uint32_t kInfMag = 0x7C00u;
   __device__ static float f(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
   __device__ static uint32_t mag(uint32_t b) { return b & 0x7FFFu; }
-  __device__ static uint32_t mag_f32(uint32_t m) { return __float_as_uint(f(m)); }
+  // Widened exactly, NaN payloads included: infinity and NaN move their
+  // mantissa bits up unchanged (a signalling NaN stays signalling, where the
+  // hardware convert would quiet it); finite values convert exactly.
+  __device__ static uint32_t mag_f32(uint32_t m) {
+    return m >= kInfMag ? 0x7F800000u | ((m & 0x3FFu) << 13) : __float_as_uint(f(m));
+  }
   __device__ static uint32_t sign(uint32_t b) { return (b >> 8) & 0x80u; }
 };
 template <>

@@ -249,7 +249,8 @@ typedef struct fp8_mm_args {
  * Each stored operand of one batch entry must span < 2^31 bytes.
  * lda >= K (NT/NN) or >= M (TN); ldb >= K (NT) or >= N (NN/TN); ldc >= N.
  * m == 0 or n == 0 launches nothing; k == 0 writes bf16(bias) (or 0).
- * c must not overlap a, b or bias. */
+ * c must not overlap a, b or bias (checked over the bytes each spans;
+ * FP8DS_EINVAL). */
 int fp8_mm(const fp8_mm_args* args, void* stream);
 
 /* fp8_mm with the workgroup tile forced: tile = index into the tile family
@@ -280,7 +281,10 @@ int fp8_mm_with_grid(const fp8_mm_args* args, int tile, int max_workgroups, void
  * zero) is skipped. */
 int fp8_mm_pair(const fp8_mm_args* first, const fp8_mm_args* second, void* stream);
 
-/* Message of the last non-zero status returned on the calling thread. */
+/* The library's own error report (not a step of the method): a message
+ * describing the last non-zero status returned on the calling thread, kept in
+ * thread-local storage until that thread's next failing call.  The pointer is
+ * owned by the library; never NULL (an empty string before any failure). */
 const char* fp8_last_error(void);
 
 #ifdef __cplusplus

@@ -16,9 +16,9 @@ astrai/extension/fp8.py):
   * the linear layer runs its forward on the congruous layout and dX / dW on
     crosswise operands (crosswise-B / crosswise-A entries).
 
-  * the bias may be stored as 8-bit codes with a scale of its own, dequantized
-    in the epilogue after the operand scaling (history of test_fp8_mma.py,
-    bias_scale entry).
+  * an 8-bit stored bias carries its own scale; it becomes a real number
+    only at the output stage, once the product has been rescaled by the
+    operands' factors (history of test_fp8_mma.py, bias_scale entry).
 
 Definition used here (the reading of "fp32 accumulate" as an approximation of
 the exact sum): for every batch b, row m, column n

@@ -8,8 +8,9 @@ What the pages fix (AstrAI commit history of astrai/extension/fp8.py,
   * each operand (x, w, g) owns a separate ring holding an amax history, a
     write index and the scale; one ring per operand keeps the amax of one
     tensor out of another's scale (FP8TensorMeta entries);
-  * one quantize call folds the tensor's amax into hist[idx], reduces the
-    window and publishes the next scale (ring-finalize entry);
+  * a single quantize call also updates the ring: the new amax goes into the
+    slot the index points at, the history is reduced to one number and the
+    scale for the following call is derived from it (ring-finalize entry);
   * the amax is taken over the values before quantization, in fp32 (the amax
     fix entry: taking it after the cast pins it near 448 and the scale at 1);
   * the GEMM dequantizes with the scale the quantize actually applied, kept

@@ -177,3 +177,75 @@ def test_mm_pair_validates_before_launch(L):
     assert L.fp8_mm_pair(ctypes.byref(first), ctypes.byref(same_c), None) == -1
     e0, e1 = args(None, None, 1 << 22, m=0), args(None, None, 1 << 25, n=0, layout=2)
     assert L.fp8_mm_pair(ctypes.byref(e0), ctypes.byref(e1), None) == 0       # both empty: nothing to do
+
+
+def test_mm_rejects_output_overlapping_an_input(L):
+    """fp8_mm's output may not share bytes with A, B or the bias (each is
+    still read while C is written); the check runs before any launch."""
+    def args(c, bias=None):
+        x = ds._MmArgs()
+        x.m, x.n, x.k = 64, 64, 64
+        x.a, x.b, x.c = 1 << 20, 1 << 21, c
+        x.a_scale_inv, x.b_scale_inv = 1 << 30, 1 << 30
+        x.lda = x.ldb = x.ldc = 64
+        if bias is not None:
+            x.bias, x.bias_kind = bias, 1
+        return x
+    for c in [(1 << 20) + 4096 - 16, (1 << 20) - 64 * 64 * 2 + 16, (1 << 21) + 2048]:   # ends in A, starts in A, in B
+        assert L.fp8_mm(ctypes.byref(args(c)), None) == -1, hex(c)
+        assert b"overlaps" in L.fp8_last_error()
+    bias = (1 << 22) + 100 * 16
+    assert L.fp8_mm(ctypes.byref(args(1 << 22, bias)), None) == -1                  # c covers the bias
+    assert b"overlaps" in L.fp8_last_error()
+    # batched: the second output entry lands on A
+    x = args((1 << 20) - 2 * 64 * 64 * 2 + 16)
+    x.batch, x.stride_a, x.stride_b, x.stride_c = 2, 64 * 64, 64 * 64, 64 * 64
+    assert L.fp8_mm(ctypes.byref(x), None) == -1
+
+
+def test_binding_checks_tensors_before_the_call():
+    """The binding refuses a tensor of the wrong dtype, a non-contiguous one, a
+    buffer shorter than the extent the kernel touches, and host memory, before
+    anything reaches the library (CPU tensors stand in for device ones)."""
+    import torch
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    with pytest.raises(ds.Fp8dsError, match="dtype"):
+        ds._need(torch.zeros(4, dtype=torch.int16), "a", ds._U8, 4)
+    with pytest.raises(ds.Fp8dsError, match="contiguous"):
+        ds._need(u8(64).view(8, 8).t(), "a", ds._U8, 8)
+    with pytest.raises(ds.Fp8dsError, match="holds 63 bytes"):
+        ds._need(u8(63), "a", ds._U8, 64)
+    with pytest.raises(ds.Fp8dsError, match="device tensor"):
+        ds._need(u8(64), "a", ds._U8, 64)
+    with pytest.raises(ds.Fp8dsError, match="is required"):
+        ds._need(None, "a", ds._U8, 64)
+    # fp8_mm's extents: NT 64 x 96 x 128 needs A 64*128, B 96*128, C 64*96 bf16
+    a, b = u8(64 * 128), u8(96 * 128)
+    out = torch.empty(64 * 96, dtype=torch.bfloat16)
+    with pytest.raises(ds.Fp8dsError, match="out holds"):
+        ds.fp8_mm(a, b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out[:-1])
+    with pytest.raises(ds.Fp8dsError, match="^a holds"):
+        ds.fp8_mm(a[:-1], b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out)
+    with pytest.raises(ds.Fp8dsError, match="^b holds"):
+        ds.fp8_mm(a, b[:-16], 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out)
+    with pytest.raises(ds.Fp8dsError, match="out has dtype"):
+        ds.fp8_mm(a, b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out.float())
+    # a padded leading dimension and a batch stride count in the extent
+    with pytest.raises(ds.Fp8dsError, match="^a holds"):
+        ds.fp8_mm(u8(63 * 144 + 127), b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, lda=144, out=out)
+    with pytest.raises(ds.Fp8dsError, match="out holds"):
+        ds.fp8_mm(u8(2 * 64 * 128), u8(2 * 96 * 128), 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30,
+                  batch=2, out=out)
+    with pytest.raises(ds.Fp8dsError, match="bias holds"):
+        ds.fp8_mm(a, b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out,
+                  bias=torch.zeros(95, dtype=torch.bfloat16))
+    with pytest.raises(ds.Fp8dsError, match="a_scale_inv has dtype"):
+        ds.fp8_mm(a, b, 0, 0, ds.NT, 64, 96, 128, torch.zeros(1, dtype=torch.float64), 1 << 30, out=out)
+    with pytest.raises(ds.Fp8dsError, match="device tensor"):       # right sizes, host memory
+        ds.fp8_mm(a, b, 0, 0, ds.NT, 64, 96, 128, 1 << 30, 1 << 30, out=out)
+    # the bias gradient's output and workspace
+    g = torch.zeros(32, 64, dtype=torch.bfloat16)
+    with pytest.raises(ds.Fp8dsError, match="out holds"):
+        ds.fp8_bias_grad(g, out=torch.empty(63, dtype=torch.bfloat16), workspace=u8(1 << 16))
+    with pytest.raises(ds.Fp8dsError, match="workspace holds"):
+        ds.fp8_bias_grad(g, out=torch.empty(64, dtype=torch.bfloat16), workspace=u8(16))

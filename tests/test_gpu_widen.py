@@ -53,6 +53,41 @@ def test_fp16_every_pattern(fmt):
         assert_ring_equal(ring.read(), ref, scale)
 
 
+@pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
+def test_fp16_signalling_nan_is_the_amax(fmt):
+    """fp16 inputs whose largest magnitude is a signalling NaN: the amax, the
+    history slot and the dynamic recipe's amax keep its payload bit for bit
+    (fp16 widens exactly, so 0x7C01 becomes 0x7F802000 and stays signalling);
+    the codes of those elements are the NaN code with their sign.  One tensor
+    per case, in the 1-D, dual and dynamic entry points."""
+    ds = require_gpu()
+    base = make_input((64, 96), 71, oracle.IN_F16)
+    cases = [
+        ("only NaN is 0x7C01", [(5, 0x7C01)]),
+        ("negative sNaN 0xFD55 above a positive 0x7C01", [(7, 0xFD55), (3000, 0x7C01)]),
+        ("a quiet 0x7E00 above an sNaN 0x7D00", [(11, 0x7D00), (12, 0x7E00)]),
+        ("sNaN 0x7DFF above an infinity", [(100, 0x7C00), (6143, 0x7DFF)]),
+    ]
+    for name, planted in cases:
+        x = base.copy().reshape(-1)
+        for pos, bits in planted:
+            x[pos] = bits
+        say(f"fp16 signalling NaN fmt={fmt}: {name}")
+        ring = ds.ScaleRing(4, fmt, 2.0)
+        q = ds.fp8_quantize(to_dev(x, oracle.IN_F16), fmt, ring)
+        codes, ref = oracle.quantize_step(oracle.ring_init(4, fmt, 2.0), x, oracle.IN_F16)
+        torch.cuda.synchronize()
+        assert np.array_equal(q.cpu().numpy(), codes), name
+        assert_ring_equal(ring.read(), ref, name)
+        ring2 = ds.ScaleRing(4, fmt, 2.0)
+        y, y_t = ds.fp8_quantize_2d(to_dev(x.reshape(64, 96), oracle.IN_F16), fmt, ring2, oracle.DUAL)
+        ry, ry_t, ref2 = oracle.quantize_step_2d(oracle.ring_init(4, fmt, 2.0), x, 64, 96, oracle.DUAL, oracle.IN_F16)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), ry) and np.array_equal(y_t.cpu().numpy(), ry_t), name
+        assert_ring_equal(ring2.read(), ref2, name)
+        check_dynamic(ds, x, oracle.IN_F16, fmt)
+
+
 @pytest.mark.parametrize("kind", [oracle.IN_F16, oracle.IN_F32])
 @pytest.mark.parametrize("fmt", [oracle.E4M3, oracle.E5M2])
 def test_input_types_ragged_chain(kind, fmt):

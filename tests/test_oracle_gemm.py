@@ -177,3 +177,113 @@ def test_entries_match_full(layout):
                           sa_rows * lda, sb_rows * ldb)
     assert np.allclose(ye, y[bi, mi, ni], rtol=1e-14, atol=0)
     assert np.array_equal(oute, out[bi, mi, ni])
+
+
+# ---------------------------------------------------------------------------
+# The acceptance helpers every GEMM verdict goes through: oracle.tolerance and
+# oracle.max_abs_dequant, against hand-derived rows (tests/golden/
+# gemm_acceptance_cases.txt).  Each mutant below is a plausible slip in one of
+# them; the rows must catch every one.
+
+import math
+
+import oracle as _oracle
+from conftest import read_golden
+
+_FMT = {"e4m3": E4M3, "e5m2": E5M2}
+
+
+def _tol_rows():
+    return [(int(r[1], 16), int(r[2]), float(r[3]), float(r[4]), float(r[5]))
+            for r in read_golden("gemm_acceptance_cases.txt") if r[0] == "tol"]
+
+
+def _mad_rows():
+    out = []
+    for r in read_golden("gemm_acceptance_cases.txt"):
+        if r[0] != "mad":
+            continue
+        codes = [] if r[3] == "-" else [int(c, 16) for c in r[3].split(",")]
+        out.append((_FMT[r[1]], float(r[2]), np.array(codes, dtype=np.uint8), float(r[4])))
+    return out
+
+
+def _tol_ok(fn):
+    return all(math.isclose(float(fn(np.array([b], dtype=np.uint16), k, ma, mb)[0]), want, rel_tol=1e-12, abs_tol=0.0)
+               for b, k, ma, mb, want in _tol_rows())
+
+
+def _mad_ok(fn):
+    return all(math.isclose(float(fn(codes, fmt, s)), want, rel_tol=1e-15, abs_tol=0.0)
+               for fmt, s, codes, want in _mad_rows())
+
+
+def test_tolerance_golden_rows():
+    rows = _tol_rows()
+    assert len(rows) >= 10
+    for b, k, ma, mb, want in rows:
+        got = float(_oracle.tolerance(np.array([b], dtype=np.uint16), k, ma, mb)[0])
+        assert math.isclose(got, want, rel_tol=1e-12, abs_tol=0.0), (hex(b), k, ma, mb, got, want)
+
+
+def test_max_abs_dequant_golden_rows():
+    rows = _mad_rows()
+    assert len(rows) >= 8
+    for fmt, s, codes, want in rows:
+        got = _oracle.max_abs_dequant(codes, fmt, s)
+        assert math.isclose(got, want, rel_tol=1e-15, abs_tol=0.0), (fmt, s, codes, got, want)
+
+
+def test_golden_rows_catch_tolerance_mutants():
+    ulp = _oracle.bf16_ulp
+    mutants = {
+        "one ulp": lambda r, k, a, b: 1.0 * ulp(r) + 1e-3 * np.sqrt(k) * a * b,
+        "K not rooted": lambda r, k, a, b: 2.0 * ulp(r) + 1e-3 * k * a * b,
+        "one maximum dropped": lambda r, k, a, b: 2.0 * ulp(r) + 1e-3 * np.sqrt(k) * a,
+        "1e-2 factor": lambda r, k, a, b: 2.0 * ulp(r) + 1e-2 * np.sqrt(k) * a * b,
+        "ulp one exponent off": lambda r, k, a, b: 4.0 * ulp(r) + 1e-3 * np.sqrt(k) * a * b,
+        "no subnormal floor": lambda r, k, a, b: 2.0 * np.where(
+            np.abs(bf16_to_f32(r)) > 0,
+            np.ldexp(1.0, np.frexp(np.where(np.abs(bf16_to_f32(r)) > 0, np.abs(bf16_to_f32(r)), 1.0))[1] - 8),
+            2.0 ** -133) + 1e-3 * np.sqrt(k) * a * b,
+        "ulp taken of the signed value": lambda r, k, a, b: 2.0 * np.where(bf16_to_f32(r) < 0, 0.0, ulp(r))
+        + 1e-3 * np.sqrt(k) * a * b,
+    }
+    assert _tol_ok(lambda r, k, a, b: _oracle.tolerance(r, k, a, b))
+    for name, fn in mutants.items():
+        assert not _tol_ok(fn), f"the golden rows do not catch the tolerance mutant '{name}'"
+
+
+def test_golden_rows_catch_max_abs_dequant_mutants():
+    def present(codes):
+        c = np.asarray(codes, dtype=np.uint8).reshape(-1)
+        return np.unique(c)
+
+    def signed_max(codes, fmt, s):
+        v = decode_fp8(present(codes), fmt)
+        return float(np.nanmax(v)) * float(np.float32(s)) if v.size else 0.0
+
+    def no_scale(codes, fmt, s):
+        v = np.abs(decode_fp8(present(codes), fmt))
+        return float(np.nanmax(v)) if v.size else 0.0
+
+    def nan_not_skipped(codes, fmt, s):
+        v = np.abs(decode_fp8(present(codes), fmt))
+        return float(np.max(v)) * float(np.float32(s)) if v.size else 0.0
+
+    def scale_not_rounded(codes, fmt, s):
+        v = np.abs(decode_fp8(present(codes), fmt))
+        return float(np.nanmax(v)) * float(s) if v.size else 0.0
+
+    def wrong_format(codes, fmt, s):
+        v = np.abs(decode_fp8(present(codes), 1 - fmt))
+        return float(np.nanmax(v)) * float(np.float32(s)) if v.size else 0.0
+
+    def divides(codes, fmt, s):
+        v = np.abs(decode_fp8(present(codes), fmt))
+        return float(np.nanmax(v)) / float(np.float32(s)) if v.size else 0.0
+
+    assert _mad_ok(_oracle.max_abs_dequant)
+    with np.errstate(invalid="ignore"):
+        for fn in (signed_max, no_scale, nan_not_skipped, scale_not_rounded, wrong_format, divides):
+            assert not _mad_ok(fn), f"the golden rows do not catch the max_abs_dequant mutant {fn.__name__}"
