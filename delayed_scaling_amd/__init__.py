@@ -14,6 +14,7 @@ Entry points (same names as the C ABI in include/fp8ds.h):
     fp8_quantize_2d(x, fmt, ring, layout, ...)       row-wise, transposed, dual
     fp8_quantize_dynamic(x, fmt, ring, out=None)     scale from x's own amax
     fp8_bias_grad(g, ..., out=None)                  column sums of a gradient
+    fp8_bias_grad_noalloc(g, ..., out=out)           the same without a workspace
     fp8_mm(a, b, ..., out=None)
     fp8_mm_pair(first, second)                       two GEMMs, one launch for dX + dW
 plus ScaleRing (a ring in a torch uint8 device tensor), BiasGradWorkspace and
@@ -107,6 +108,8 @@ def lib():
         L.fp8_bias_grad_workspace_bytes.argtypes = [i64, i64]
         L.fp8_bias_grad.restype = i32
         L.fp8_bias_grad.argtypes = [vp, i64, i64, i32, vp, i32, vp, vp, vp]
+        L.fp8_bias_grad_noalloc.restype = i32
+        L.fp8_bias_grad_noalloc.argtypes = [vp, i64, i64, i32, vp, i32, vp, vp]
         L.fp8_last_error.restype = ctypes.c_char_p
         L.fp8_last_error.argtypes = []
         _lib = L
@@ -360,6 +363,36 @@ def fp8_bias_grad(g, rows=None, cols=None, fmt=None, g_scale_inv=None, out_f32=F
     return out
 
 
+NOALLOC_MAX_BYTES = 1 << 20   # FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES
+
+
+def fp8_bias_grad_noalloc(g, rows=None, cols=None, fmt=None, g_scale_inv=None, out_f32=False,
+                          out=None, stream=None):
+    """fp8_bias_grad without a workspace (the library's own device scratch),
+    for callers that cannot allocate; `out` must then be given.  Shapes whose
+    workspace would exceed NOALLOC_MAX_BYTES are refused by the library."""
+    if g.dim() == 2 and rows is None:
+        rows, cols = g.shape
+    if g.dtype == torch.uint8:
+        if fmt is None:
+            raise Fp8dsError("uint8 gradients need fmt")
+        g_type = G_E4M3 if int(fmt) == E4M3 else G_E5M2
+    else:
+        g_type = {torch.bfloat16: G_BF16, torch.float16: G_F16, torch.float32: G_F32}.get(g.dtype)
+        if g_type is None:
+            raise Fp8dsError("g must be bf16, fp16, fp32 or uint8 codes")
+    esize = {G_E4M3: 1, G_E5M2: 1, G_F32: 4}.get(g_type, 2)
+    _need(g, "g", (g.dtype,), int(rows) * int(cols) * esize, device=False)
+    out_dtype = torch.float32 if out_f32 else torch.bfloat16
+    _need(out, "out", (out_dtype,), int(cols) * (4 if out_f32 else 2), device=False)
+    if g_type in (G_E4M3, G_E5M2) and isinstance(g_scale_inv, torch.Tensor):
+        _need(g_scale_inv, "g_scale_inv", _F32, 4, device=False)
+    _on_device(("g", g), ("out", out), ("g_scale_inv", g_scale_inv))
+    _check(lib().fp8_bias_grad_noalloc(_ptr(g), int(rows), int(cols), g_type, _addr(g_scale_inv),
+                                       int(bool(out_f32)), _ptr(out), _stream(stream)))
+    return out
+
+
 def _addr(x):
     if x is None:
         return None
@@ -454,6 +487,7 @@ def fp8_mm_pair(first, second, stream=None):
 
 
 __all__ = ["E4M3", "E5M2", "NT", "NN", "TN", "TILES", "Fp8dsError", "ScaleRing", "fp8_mm", "fp8_mm_pair",
-           "fp8_quantize", "fp8_quantize_batch", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad", "BiasGradWorkspace",
+           "fp8_quantize", "fp8_quantize_batch", "fp8_quantize_2d", "fp8_quantize_dynamic", "fp8_bias_grad",
+           "fp8_bias_grad_noalloc", "BiasGradWorkspace",
            "bias_grad_workspace_bytes", "lib", "read_ring", "scale_ring_bytes", "scale_ring_init", "LIB_PATH",
            "IN_BF16", "IN_F16", "IN_F32", "ROWWISE", "TRANSPOSED", "DUAL"]

@@ -59,6 +59,31 @@ int check_quantize(const char* fn, const void* x, int64_t numel, int in_type, in
 }
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 
+// Checks shared by the two bias-gradient entry points; FP8DS_OK with
+// *nothing set when there is nothing to do (no columns).
+int check_bias_grad(const char* fn, const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv,
+                    const void* out, bool need_workspace, const void* workspace, bool* nothing) {
+  *nothing = false;
+  if (g_type < FP8DS_G_BF16 || g_type > FP8DS_G_E5M2) return set_error(FP8DS_EINVAL, "%s: bad g_type %d", fn, g_type);
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+    return set_error(FP8DS_EINVAL, "%s: rows and cols must be in [0, 2^31)", fn);
+  if (cols == 0) {
+    *nothing = true;
+    return FP8DS_OK;
+  }
+  if (!out || (need_workspace && !workspace) || (rows > 0 && !g))
+    return set_error(FP8DS_EINVAL, "%s: g, out or workspace is NULL", fn);
+  const bool codes = g_type == FP8DS_G_E4M3 || g_type == FP8DS_G_E5M2;
+  if (codes && !g_scale_inv) return set_error(FP8DS_EINVAL, "%s: 8-bit g needs g_scale_inv", fn);
+  if (cols & 7) return set_error(FP8DS_EALIGN, "%s: cols %lld is not a multiple of 8", fn, (long long)cols);
+  if ((rows > 0 && !aligned16(g)) || (need_workspace && !aligned16(workspace)))
+    return set_error(FP8DS_EALIGN, "%s: g or workspace not 16-byte aligned", fn);
+  const int64_t esize = g_type == FP8DS_G_F32 ? 4 : codes ? 1 : 2;
+  if (rows * cols * esize >= (int64_t)1 << 40) return set_error(FP8DS_EUNSUPPORTED, "%s: g too large", fn);
+  return FP8DS_OK;
+}
+
+
 // Largest byte offset + 1 that one batch entry of a stored [rows][cols] view
 // with leading dimension ld touches, rounded up to 16.
 int64_t view_extent(int64_t rows, int64_t cols, int64_t ld) {
@@ -272,21 +297,24 @@ size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols) {
 
 int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv, int out_f32,
                   void* out, void* workspace, void* stream) {
-  const char* fn = "fp8_bias_grad";
-  if (g_type < FP8DS_G_BF16 || g_type > FP8DS_G_E5M2) return set_error(FP8DS_EINVAL, "%s: bad g_type %d", fn, g_type);
-  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
-    return set_error(FP8DS_EINVAL, "%s: rows and cols must be in [0, 2^31)", fn);
-  if (cols == 0) return FP8DS_OK;
-  if (!out || !workspace || (rows > 0 && !g)) return set_error(FP8DS_EINVAL, "%s: g, out or workspace is NULL", fn);
-  const bool codes = g_type == FP8DS_G_E4M3 || g_type == FP8DS_G_E5M2;
-  if (codes && !g_scale_inv) return set_error(FP8DS_EINVAL, "%s: 8-bit g needs g_scale_inv", fn);
-  if (cols & 7) return set_error(FP8DS_EALIGN, "%s: cols %lld is not a multiple of 8", fn, (long long)cols);
-  if ((rows > 0 && !aligned16(g)) || !aligned16(workspace))
-    return set_error(FP8DS_EALIGN, "%s: g or workspace not 16-byte aligned", fn);
-  const int64_t esize = g_type == FP8DS_G_F32 ? 4 : codes ? 1 : 2;
-  if (rows * cols * esize >= (int64_t)1 << 40) return set_error(FP8DS_EUNSUPPORTED, "%s: g too large", fn);
+  bool nothing = false;
+  if (const int st = check_bias_grad("fp8_bias_grad", g, rows, cols, g_type, g_scale_inv, out, true, workspace,
+                                     &nothing))
+    return st;
+  if (nothing) return FP8DS_OK;
   return launch_bias_grad(g, (int)rows, (int)cols, g_type, g_scale_inv, out_f32 != 0, out, workspace,
                           static_cast<hipStream_t>(stream));
+}
+
+int fp8_bias_grad_noalloc(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv,
+                          int out_f32, void* out, void* stream) {
+  bool nothing = false;
+  if (const int st = check_bias_grad("fp8_bias_grad_noalloc", g, rows, cols, g_type, g_scale_inv, out, false,
+                                     nullptr, &nothing))
+    return st;
+  if (nothing) return FP8DS_OK;
+  return launch_bias_grad_noalloc(g, (int)rows, (int)cols, g_type, g_scale_inv, out_f32 != 0, out,
+                                  static_cast<hipStream_t>(stream));
 }
 
 int fp8_mm(const fp8_mm_args* a, void* stream) { return fp8_mm_with_grid(a, -1, 0, stream); }

@@ -25,6 +25,10 @@ int launch_amax(const void* x, int64_t numel, int in_type, int fmt, void* ring, 
 size_t bias_grad_workspace(int64_t rows, int64_t cols);
 int launch_bias_grad(const void* g, int rows, int cols, int g_type, const float* g_scale_inv, int out_f32, void* out,
                      void* workspace, hipStream_t stream);
+// The bias gradient with its scratch in the library's own device array (no
+// workspace argument, nothing allocated); FP8DS_EUNSUPPORTED past its size.
+int launch_bias_grad_noalloc(const void* g, int rows, int cols, int g_type, const float* g_scale_inv, int out_f32,
+                             void* out, hipStream_t stream);
 
 struct GemmProblem {
   const uint8_t* a;

@@ -19,6 +19,8 @@
 // ticket, then a top-level max + ticket); the block holding the last
 // top-level ticket finalizes the ring and every scratch word is back at zero
 // for the next call on the same stream.
+#include <atomic>
+
 #include "device_common.h"
 #include "fp8ds.h"
 #include "launch.h"
@@ -848,6 +850,75 @@ int launch_bias_grad(const void* g, int rows, int cols, int g_type, const float*
                      static_cast<const uint8_t*>(g), rows, cols, slices, rps, g_scale_inv, out_f32, out, partial,
                      tickets);
   return check_launch("bias_grad_kernel");
+}
+
+
+// ---------------------------------------------------------------------------
+// The bias gradient without a caller workspace, for callers that cannot
+// allocate: its tickets and partial sums live in `scratch`, a device array of
+// this file that every GPU the library runs on holds until the process ends.
+// Host code never passes the array's name to a kernel (on the host that name
+// is only a stand-in): each device's address is looked up once with
+// hipGetSymbolAddress, with that device current, and kept per device.
+
+static __device__ __align__(256) uint8_t scratch[FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::atomic<bool> g_scratch_clear[kMaxDevices];
+
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+// The current device's copy of `scratch`, or nullptr (with the error set).
+void* scratch_address(int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error(FP8DS_ELAUNCH, "fp8_bias_grad_noalloc: no usable current device");
+    return nullptr;
+  }
+  *dev_out = dev;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    set_error(FP8DS_ELAUNCH, "fp8_bias_grad_noalloc: hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+int launch_bias_grad_noalloc(const void* g, int rows, int cols, int g_type, const float* g_scale_inv, int out_f32,
+                             void* out, hipStream_t stream) {
+  const size_t need = bias_grad_workspace(rows, cols);
+  if (need > (size_t)FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES)
+    return set_error(FP8DS_EUNSUPPORTED,
+                     "fp8_bias_grad_noalloc: a %d x %d gradient needs %zu bytes of scratch, more than the %d the "
+                     "library holds (use fp8_bias_grad with a workspace)",
+                     rows, cols, need, FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES);
+  int dev = 0;
+  void* ws = scratch_address(&dev);
+  if (!ws) return FP8DS_ELAUNCH;
+  // The kernel leaves its scratch all zero after every call; the first call
+  // on a device zeroes the ticket words (a fill kernel on the caller's stream,
+  // so it can be captured).  While the stream is capturing, the clear goes
+  // into the graph and the next call clears again.
+  if (!g_scratch_clear[dev].load(std::memory_order_acquire)) {
+    const int words = (int)(bias_grad_tickets_bytes(cols) / 4);
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), words);
+    if (const int st = check_launch("clear_words_kernel")) return st;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+      g_scratch_clear[dev].store(true, std::memory_order_release);
+  }
+  return launch_bias_grad(g, rows, cols, g_type, g_scale_inv, out_f32, out, ws, stream);
 }
 
 }  // namespace fp8ds

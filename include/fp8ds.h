@@ -220,6 +220,25 @@ size_t fp8_bias_grad_workspace_bytes(int64_t rows, int64_t cols);
 int fp8_bias_grad(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv, int out_f32,
                   void* out, void* workspace, void* stream);
 
+/* fp8_bias_grad for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results (bit for bit) and errors
+ * as fp8_bias_grad, without `workspace`: the tickets and partial sums live in
+ * a device array of the library, FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES bytes per
+ * GPU, held from the first call on that GPU until the process ends.  A shape
+ * whose fp8_bias_grad_workspace_bytes exceeds that size is
+ * FP8DS_EUNSUPPORTED (with 1 MiB: any rows with cols up to 2^17, or cols up
+ * to about 2.6e5 with few rows).  Nothing is allocated and nothing
+ * synchronizes.  All calls on one GPU share the array: calls that may overlap
+ * on one GPU (other streams, other threads) race and give undefined results;
+ * order them on one stream.  The first call on a GPU also clears the array's
+ * ticket words (one small kernel on `stream`; repeated while the stream is
+ * capturing, so a captured graph clears them too); every call leaves the
+ * array zero again. */
+#define FP8DS_BIAS_GRAD_NOALLOC_MAX_BYTES (1 << 20)
+int fp8_bias_grad_noalloc(const void* g, int64_t rows, int64_t cols, int g_type, const float* g_scale_inv,
+                          int out_f32, void* out, void* stream);
+
 /* Scaled FP8 GEMM arguments.  Zero-initialise and set what you use: a
  * zeroed field means "absent" (gemm.cuh history @5e76fbd1, null-default
  * params entry). */

@@ -11,7 +11,7 @@ import torch
 import oracle
 from gpu_util import bf16_bits, require_gpu, say, to_dev_bf16, to_dev_u8
 from synth import bf16_normal, random_codes, seed_for
-from test_gpu_configs import check_mm
+from test_gpu_configs import check_mm, check_mm_tiles
 from test_gpu_gemm import FINITE, scale_tensor
 from test_gpu_quantize import assert_ring_equal
 from test_gpu_widen import make_input, to_dev
@@ -86,18 +86,20 @@ def test_bias_grad_at_full_size():
     assert int(ws.buf.count_nonzero()) == 0                 # the workspace is clear again
 
 
-@pytest.mark.parametrize("layout", [oracle.NN, oracle.TN])
-def test_backward_layouts_at_full_size(layout):
+@pytest.mark.parametrize("layout,fa", [(oracle.NT, oracle.E4M3), (oracle.NN, oracle.E5M2), (oracle.TN, oracle.E5M2)])
+def test_layouts_at_full_size(layout, fa):
+    """8192^3 in the forward (NT, E4M3 x E4M3) and backward (NN / TN, E5M2 x
+    E4M3) formats: two whole rows and two whole columns of every 256 x 256
+    output tile against the oracle."""
     ds = require_gpu()
-    a = random_codes((N, N), 4100 + layout, FINITE[oracle.E5M2])
+    a = random_codes((N, N), 4100 + layout, FINITE[fa])
     b = random_codes((N, N), 4200 + layout, FINITE[oracle.E4M3])
     sa, sb = 0.0119, 0.0227
     say(f"full-size GEMM layout {layout}")
-    y = ds.fp8_mm(to_dev_u8(a), to_dev_u8(b), oracle.E5M2, oracle.E4M3, layout, N, N, N, scale_tensor(sa),
+    y = ds.fp8_mm(to_dev_u8(a), to_dev_u8(b), fa, oracle.E4M3, layout, N, N, N, scale_tensor(sa),
                   scale_tensor(sb))
     torch.cuda.synchronize()
-    check_mm(ds, y, a.reshape(-1), b.reshape(-1), oracle.E5M2, oracle.E4M3, layout, N, N, N, sa, sb, sample=200,
-             what=f"8192^3 layout {layout}")
+    check_mm_tiles(ds, y, a, b, fa, oracle.E4M3, layout, N, N, N, sa, sb, what=f"8192^3 layout {layout}")
 
 
 def test_bias_gemm_at_full_size():
@@ -119,5 +121,5 @@ def test_bias_gemm_at_full_size():
                    scale_tensor(sb), tile=0, **kw)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
-    check_mm(ds, y, a.reshape(-1), b.reshape(-1), oracle.E4M3, oracle.E4M3, oracle.NT, m, n, k, sa, sb, bias=bias,
-             sample=300, what="8192x8192x1024 NT with bias")
+    check_mm_tiles(ds, y, a, b, oracle.E4M3, oracle.E4M3, oracle.NT, m, n, k, sa, sb, bias=bias,
+                   what="8192x8192x1024 NT with bias")

@@ -287,3 +287,22 @@ def test_golden_rows_catch_max_abs_dequant_mutants():
     with np.errstate(invalid="ignore"):
         for fn in (signed_max, no_scale, nan_not_skipped, scale_not_rounded, wrong_format, divides):
             assert not _mad_ok(fn), f"the golden rows do not catch the max_abs_dequant mutant {fn.__name__}"
+
+
+def test_identity_products_are_exact_decoded_codes():
+    """The premise of the GPU's bit-exact identity GEMMs: with one operand the
+    identity (code of 1.0 on the diagonal) every output is one product, and
+    with scales 1 or 0.75 * 0.125 each is the decoded code times the scales,
+    exactly (at most 6 significant bits, so the one bf16 rounding is exact)."""
+    one = {E4M3: 0x38, E5M2: 0x3C}
+    for fmt in (E4M3, E5M2):
+        codes = np.array(FINITE[fmt], np.uint8)
+        a = codes[(np.arange(256)[:, None] + np.arange(256)[None, :]) % len(codes)]
+        eye = np.zeros((256, 256), np.uint8)
+        eye[np.arange(256), np.arange(256)] = one[fmt]
+        for sa, sb in [(1.0, 1.0), (0.75, 0.125)]:
+            want = decode_fp8(a, fmt) * sa * sb
+            _, ref = mm(a, eye, fmt, fmt, NN, 256, 256, 256, 256, 256, sa, sb)
+            assert np.array_equal(bf16_to_f32(ref[0]).astype(np.float64), want)
+            _, ref = mm(eye, a, fmt, fmt, NN, 256, 256, 256, 256, 256, sa, sb)
+            assert np.array_equal(bf16_to_f32(ref[0]).astype(np.float64), want)
