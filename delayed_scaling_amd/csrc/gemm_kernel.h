@@ -211,12 +211,22 @@ __device__ __forceinline__ void wait_stages(int stages) {
 }
 
 // Workgroup barrier ordering LDS only: outstanding global->LDS prefetches of
-// later stages stay in flight across it.
+// later stages stay in flight across it.  It waits for this wave's own LDS
+// operations first (the release half), so LDS written before it is seen by
+// every wave after it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// The K loop's per-stage barrier: a bare s_barrier that keeps the compiler
+// from moving memory operations across it but waits for nothing, so LDS
+// reads already issued stay in flight across it.  The callers make the
+// data it publishes complete first (they wait for the global -> LDS loads of
+// the stage by vmcnt), and never write LDS that another wave may still read
+// (see the buffer rotation in gemm_body).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Lanes l and l+32 hold the same row; lane l+32 holds the four columns after
 // lane l's in each 8-column group.  This swaps a value between the two lane
@@ -479,7 +489,7 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TN][TM]) {
 // Global -> LDS side of a workgroup that runs the output tiles wg, wg + G,
 // ... (wg its index among the G workgroups of its problem) as one stream of K
 // stages of kBK bytes.
-// Stage s lands in LDS buffer s % kStages as [A tile | B tile]; each of the
+// Stage s lands in LDS buffer s % NBUF as [A tile | B tile]; each of the
 // NW waves brings 1 KiB per buffer_load ... lds.  The next stage to issue is
 // stage k of the workgroup's tile number it.  Each tile's operand strips get
 // one buffer descriptor spanning the rest of the operand from the strip's
@@ -487,7 +497,7 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TN][TM]) {
 // workgroup's last tile the descriptors are empty: those loads fetch nothing
 // and land zeros, so every stage issues the same number of loads and vmcnt
 // counts stay fixed.
-template <int BM, int BN, int NW, int kStages, bool A_KC, bool B_KC>
+template <int BM, int BN, int NW, int NBUF, bool A_KC, bool B_KC>
 struct TileLoader {
   static constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK, STAGE = A_BYTES + B_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / NW, B_LOADS = B_BYTES / 1024 / NW;
@@ -541,7 +551,7 @@ struct TileLoader {
     Ctx c;
     c.sa = A_KC ? k0 : k0 * p.lda;
     c.sb = B_KC ? k0 : k0 * p.ldb;
-    c.la = lds_address(smem + (s % kStages) * STAGE) + wave * 1024;
+    c.la = lds_address(smem + (s % NBUF) * STAGE) + wave * 1024;
     c.lb = c.la + A_BYTES;
     c.tail = k >= kt_full;
     return c;
@@ -607,6 +617,17 @@ __device__ __forceinline__ void read_frags(const lds_char_t* stage_buf, int r0, 
   for (int i = 0; i < TN; ++i) fb[i] = load_frag<B_KC, BN>(sb, c0 + i * 32, lane);
 }
 
+// Items of one kind (global loads, or fragment reads) issued after MFMA q of
+// a stage's nm MFMAs, as the half-open range [slot_items(q), slot_items(q+1)):
+// the n items spread evenly over the MFMAs of one parity (q % 2 == parity),
+// so loads and fragment reads take turns after successive MFMAs.  A stage of
+// one MFMA issues everything after it.
+constexpr int slot_items(int q, int nm, int n, int parity) {
+  if (nm == 1) return q == 0 ? 0 : n;
+  const int slots = (nm + 1 - parity) / 2;    // MFMAs of this parity
+  return (q + 1 - parity) / 2 * n / slots;    // items issued before MFMA q
+}
+
 template <int TM, int TN, int FA, int FB>
 __device__ __forceinline__ void mfmas(v16f (&acc)[TN][TM], const v8i (&fa)[TM], const v8i (&fb)[TN]) {
 #pragma unroll
@@ -617,20 +638,28 @@ __device__ __forceinline__ void mfmas(v16f (&acc)[TN][TM], const v8i (&fa)[TM], 
 }
 
 // General kernel: any tile of the family, any K.  Waves in a WGM x WGN grid
-// each own a (BM/WGM) x (BN/WGN) block of the tile.  Every wave runs all
-// stages: wait for stage s+1, barrier, then stage s's MFMAs interleaved with
-// the loads of stage s+kStages and the LDS reads of stage s+1's fragments.
-template <int BM, int BN, int kStages>
-constexpr int smem_bytes() { return kStages * (BM + BN) * kBK; }
+// each own a (BM/WGM) x (BN/WGN) block of the tile.  The workgroup has NBUF
+// LDS stage buffers and keeps D = NBUF - 1 stages of global loads in flight.
+// Every wave runs all stages: wait for stage s+1, barrier, then stage s's
+// MFMAs interleaved with the loads of stage s+D and the LDS reads of stage
+// s+1's fragments.
+template <int BM, int BN, int NBUF>
+constexpr int smem_bytes() { return NBUF * (BM + BN) * kBK; }
 
 // Workgroup wg of the G that run one problem (a whole launch, or one part of
 // a launch shared by two problems); smem: the workgroup's LDS stages.
-template <int BM, int BN, int WGM, int WGN, int kStages, bool A_KC, bool B_KC, int FA, int FB>
+template <int BM, int BN, int WGM, int WGN, int NBUF, bool A_KC, bool B_KC, int FA, int FB>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, int wg, int G) {
   constexpr int NW = WGM * WGN, kThreads = 64 * NW;   // waves in a WGM x WGN grid
   constexpr int WM = BM / WGM, WN = BN / WGN;          // C block of one wave
   constexpr int TM = WM / 32, TN = WN / 32;
-  using Loader = TileLoader<BM, BN, NW, kStages, A_KC, B_KC>;
+  // Stages of global loads in flight.  The loads issued during stage s fill
+  // stage s+D's buffer, which held stage s-1: every wave consumed that
+  // stage's fragments in its MFMAs before the barrier that opened stage s,
+  // so the barrier need not wait for LDS reads still in flight.
+  constexpr int D = NBUF - 1;
+  static_assert(D >= 2, "at least two stages in flight");
+  using Loader = TileLoader<BM, BN, NW, NBUF, A_KC, B_KC>;
   constexpr int STAGE = Loader::STAGE, LPS = Loader::LPS;
   static_assert(TM >= 1 && TN >= 1, "tile too small");
 
@@ -666,7 +695,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 
   Loader ld;
   ld.init(p, wave, lane, kt_full, wg, G);
-  auto buf = [&](uint32_t st) __attribute__((always_inline)) { return smem + (st % kStages) * STAGE; };
+  auto buf = [&](uint32_t st) __attribute__((always_inline)) { return smem + (st % NBUF) * STAGE; };
 
   // Stage s+1 is visible to the whole workgroup: zero its K padding first if
   // it is a tail stage (K position next_k) of a K that is not a multiple of 16.
@@ -679,23 +708,29 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 
   // Fragments of two consecutive stages live in registers: while the MFMAs
   // of stage s run, the LDS reads of stage s+1 and the global loads of stage
-  // s+kStages are in flight.
+  // s+D are in flight.
   v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
-  // One stage s: make stage s+1 visible, then issue stage s's MFMAs one by
-  // one, each followed, when READ, by its share of the global loads of stage
-  // s+kStages (into the buffer stage s freed) and of the LDS reads of stage
-  // s+1's fragments into na / nb.  Scheduling barriers keep that interleave:
-  // bursts of loads or LDS reads right after the barrier left the matrix cores
-  // idle.  The wave runs at raised priority while it issues the MFMA stream.
-  // A tile's last stage (not READ) issues MFMAs only: its buffer stages the
-  // epilogue, and its loads go out after it.
+  // One stage s: make stage s+1 visible (its loads have landed for every
+  // wave), then issue stage s's MFMAs one by one, each followed, when READ,
+  // by its share of the global loads of stage s+D (into the buffer stage s-1
+  // freed) and of the LDS reads of stage s+1's fragments into na / nb.  The
+  // barrier does not wait for this wave's LDS reads: the fragments of stage
+  // s+1 are waited for where its MFMAs use them, the first ones read first.
+  // Scheduling barriers keep that interleave: bursts of loads or LDS reads
+  // right after the barrier left the matrix cores idle.  The wave runs at
+  // raised priority while it issues the MFMA stream.  A tile's last stage
+  // (not READ) issues MFMAs only: the buffer its loads would fill stages the
+  // epilogue, and those loads go out after it.
   constexpr int NM = TM * TN, NF = TM + TN;
   auto stage = [&](auto read, int s, int next_k, const v8i (&fa)[TM], const v8i (&fb)[TN], v8i (&na)[TM],
                    v8i (&nb)[TN]) __attribute__((always_inline)) {
     constexpr bool READ = decltype(read)::value;
-    wait_stages<LPS, kStages>(kStages - 2);
-    lds_barrier();
+    // Global loads after the even-numbered MFMAs, fragment reads after the
+    // odd ones (a stage of one MFMA issues both after it).
+    constexpr int LP = 0, FP = NM == 1 ? 0 : 1;
+    wait_stages<LPS, NBUF>(D - 2);
+    stage_barrier();
     fix_tail(s, next_k);
     const typename Loader::Ctx c = ld.ctx(p, smem, wave, kt_full);
     const lds_char_t* sa = buf(s + 1);
@@ -707,9 +742,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       if constexpr (READ) {
 #pragma unroll
-        for (int l = q * LPS / NM; l < (q + 1) * LPS / NM; ++l) ld.issue_one(c, l);
+        for (int l = slot_items(q, NM, LPS, LP); l < slot_items(q + 1, NM, LPS, LP); ++l) ld.issue_one(c, l);
 #pragma unroll
-        for (int f = q * NF / NM; f < (q + 1) * NF / NM; ++f) {
+        for (int f = slot_items(q, NM, NF, FP); f < slot_items(q + 1, NM, NF, FP); ++f) {
           if (f < TM) na[f] = load_frag<A_KC, BM>(sa, r0 + f * 32, lane);
           else nb[f - TM] = load_frag<B_KC, BN>(sb, c0 + (f - TM) * 32, lane);
         }
@@ -722,11 +757,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   using Read = std::true_type;
   using NoRead = std::false_type;
 
-  // Prologue: stages 0 .. kStages-1 in flight, stage 0's fragments in set 0.
+  // Prologue: stages 0 .. D-1 in flight, stage 0's fragments in set 0.
 #pragma unroll
-  for (int st = 0; st < kStages; ++st) ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
+  for (int st = 0; st < D; ++st) ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
   const float alpha = make_alpha();
-  wait_stages<LPS, kStages>(kStages - 1);
+  wait_stages<LPS, NBUF>(D - 1);
   lds_barrier();
   if (kfix && kt_full == 0) {
     zero_k_padding<BM, BN, A_KC, B_KC, kThreads>(buf(0), p.k, kt_full);
@@ -738,9 +773,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   // kt_total - 1 leading stages in pairs that alternate the two fragment
   // sets (one single stage first when their count is odd, its fragments
   // moved back to set 0).  Its last stage runs the MFMAs only; then the tile
-  // is stored through that stage's buffer, the stage's loads go out, the
-  // accumulators are cleared and the next stage's fragments read into set 0,
-  // so the epilogue has the registers of both fragment sets to itself.
+  // is stored through the buffer that stage's loads fill (stage s0 +
+  // kt_total - 1 + D's, free since the barrier that opened the stage), the
+  // loads go out, the accumulators are cleared and the next stage's
+  // fragments read into set 0, so the epilogue has the registers of both
+  // fragment sets to itself.
+
   for (int it = 0; it < my_tiles; ++it) {
     const int s0 = it * kt_total;
     int kt = 0;
@@ -757,7 +795,8 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
       stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
     }
     stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
-    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, buf(s0 + kt_total - 1));
+    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha,
+                                          buf(s0 + kt_total - 1 + D));
     // The staging reads have returned before the loads refill the area.  (The
     // loads after the last tile fetch nothing; skipping them with an early
     // exit made the compiler wait for every outstanding load in the K loop.)
@@ -772,11 +811,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 }
 
 // One problem per launch: workgroup blockIdx.x of gridDim.x.
-template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC, bool B_KC, int FA, int FB>
+template <int BM, int BN, int WGM, int WGN, int NBUF, int OCC, bool A_KC, bool B_KC, int FA, int FB>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, kStages>()];
-  gemm_body<BM, BN, WGM, WGN, kStages, A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x,
-                                                          (int)gridDim.x);
+  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, NBUF>()];
+  gemm_body<BM, BN, WGM, WGN, NBUF, A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x,
+                                                       (int)gridDim.x);
 }
 
 // Two independent problems in one launch (a layer's dX and dW): workgroups
@@ -785,15 +824,15 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
 // operand orientations differ.  g0 is a multiple of 8 whenever the first
 // problem's workgroups run more than one tile each, so the second keeps the
 // tile-to-XCD mapping of a launch of its own.
-template <int BM, int BN, int WGM, int WGN, int kStages, int OCC, bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1,
+template <int BM, int BN, int WGM, int WGN, int NBUF, int OCC, bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1,
           int FA, int FB>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_pair_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, kStages>()];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, NBUF>()];
   const int wg = (int)blockIdx.x;
   if (wg < g0)
-    gemm_body<BM, BN, WGM, WGN, kStages, A_KC0, B_KC0, FA, FB>(p0, (lds_char_t*)smem_raw, wg, g0);
+    gemm_body<BM, BN, WGM, WGN, NBUF, A_KC0, B_KC0, FA, FB>(p0, (lds_char_t*)smem_raw, wg, g0);
   else
-    gemm_body<BM, BN, WGM, WGN, kStages, A_KC1, B_KC1, FA, FB>(p1, (lds_char_t*)smem_raw, wg - g0,
+    gemm_body<BM, BN, WGM, WGN, NBUF, A_KC1, B_KC1, FA, FB>(p1, (lds_char_t*)smem_raw, wg - g0,
                                                               (int)gridDim.x - g0);
 }
 
