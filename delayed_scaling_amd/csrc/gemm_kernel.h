@@ -618,12 +618,13 @@ __device__ __forceinline__ void read_frags(const lds_char_t* stage_buf, int r0, 
 }
 
 // Items of one kind (global loads, or fragment reads) issued after MFMA q of
-// a stage's nm MFMAs, as the half-open range [slot_items(q), slot_items(q+1)):
-// the n items spread evenly over the MFMAs of one parity (q % 2 == parity),
-// so loads and fragment reads take turns after successive MFMAs.  A stage of
-// one MFMA issues everything after it.
+// a stage, as the half-open range [slot_items(q), slot_items(q+1)): the n
+// items spread evenly over the first nm MFMAs of one parity (q % 2 ==
+// parity), so loads and fragment reads take turns after successive MFMAs.  A
+// stage of one MFMA issues everything after it.
 constexpr int slot_items(int q, int nm, int n, int parity) {
   if (nm == 1) return q == 0 ? 0 : n;
+  if (q > nm) q = nm;                         // MFMAs past the first nm issue none
   const int slots = (nm + 1 - parity) / 2;    // MFMAs of this parity
   return (q + 1 - parity) / 2 * n / slots;    // items issued before MFMA q
 }
@@ -810,12 +811,323 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
+// ---------------------------------------------------------------------------
+// The four-wave 256x256 tile on load units of 128 K bytes.
+//
+// An LDS-direct load that covers 128 contiguous bytes of each of 8 rows moves
+// more bytes per cycle through the CU's address unit than one that covers 64
+// bytes of 16 rows (measured on gfx950, with the fragment reads of a GEMM
+// running beside the loads: 40 against 36 bytes per clock per CU).  At this
+// tile the loads take about a third of the CU's load throughput, so queueing
+// there stalled the waves' instruction streams, and with them the MFMAs.
+//
+// Here the operands move through LDS in units of 128 K bytes.  A "load stage"
+// brings one operand's 256 rows (or K rows, crosswise) of one unit, 32 KiB, 8
+// loads per wave; a unit's A and B are consecutive load stages, A first, and
+// load stage j lands in slot j % 5 of a ring of five 32 KiB slots.  The MFMAs
+// still run half-stages of 64 K bytes, reading the fragments of each half
+// during the half before, and half-stage t issues load stage t + 4, whose
+// slot held load stage t - 1.  So:
+//  * at an odd half-stage t = 2U - 1 (about to read unit U's first half) the
+//    wave waits until only load stage 2U + 2 may be in flight, i.e. unit U
+//    has landed, and the workgroup meets at a barrier that also waits for its
+//    LDS reads; no other half-stage waits or meets;
+//  * the slot load stage t + 4 refills held load stage t - 1, whose last
+//    fragment reads were issued in half-stage t - 2 at the latest and are
+//    complete at the barrier of t - 1 or t;
+//  * unit U's B has one to two half-stages from issue to use, its A two to
+//    three.
+// The tile's half-stages come in pairs (even: A loads, reads the unit's second
+// half; odd: B loads, reads the next unit's first half), so the operand a
+// stage loads and the fragment sets are fixed at compile time.  K tails: a
+// unit past K loads zeros; the chunk holding K's end is zeroed past K in the
+// K-contiguous slots of a tile's last unit, as in the general kernel.
+
+constexpr int kKU = 128;      // K bytes per load unit
+constexpr int kUSlots = 5;    // slots of the ring
+
+// K-contiguous slot [rows][128 B]: chunk c (0..7) of row r sits at chunk
+// c ^ swz_k128(r).  Eight consecutive rows' reads of one chunk then cover
+// 32 distinct banks (each half of a row's chunks stays in its half).
+__device__ __forceinline__ int swz_k128(int r) { return (r >> 1) & 3; }
+
+// 32 rows x 64 k (half h of the unit) of a K-contiguous slot: lane l gets row
+// base + l % 32, k = 64 h + 32 (l / 32) + [0, 32).
+__device__ __forceinline__ v8i frag_k128(const lds_char_t* slot, int base, int lane, int h) {
+  const int row = base + (lane & 31);
+  const int c0 = 4 * h + 2 * (lane >> 5);
+  const int sw = swz_k128(row);
+  const v4i lo = *(const lds_v4i_t*)(slot + row * kKU + ((c0 ^ sw) << 4));
+  const v4i hi = *(const lds_v4i_t*)(slot + row * kKU + (((c0 + 1) ^ sw) << 4));
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// The same fragment from a crosswise slot [128 k][256 B]: half h is k rows
+// 64 h .. 64 h + 63, read as in the general kernel.
+template <bool KC>
+__device__ __forceinline__ v8i frag_u128(const lds_char_t* slot, int base, int lane, int h) {
+  if constexpr (KC) return frag_k128(slot, base, lane, h);
+  else return frag_mn<16>(slot + h * 64 * 256, base, lane);
+}
+
+// Load l of a wave covers slots i = (l * NW + wave) * 64 + lane: for a
+// K-contiguous operand rows 32 l + 8 wave + lane / 8, chunk lane % 8; for a
+// crosswise one k rows 16 l + 4 wave + lane / 16, chunk lane % 16.  The
+// swizzle depends only on the row bits that l leaves alone, so a lane's byte
+// offset is base + l * step with one per-lane base and a uniform step.
+// Rows of a K-contiguous operand past M (N) start past the end of the
+// operand, where the buffer descriptor's range check returns zeros; columns
+// of a crosswise operand past N (M) are marked kOOB in the base.
+template <bool KC, int NW>
+__device__ __forceinline__ uint32_t u128_base(int wave, int lane, int mn0, int mn_lim, uint32_t ld) {
+  if constexpr (KC) {
+    const int row = 8 * wave + (lane >> 3), lch = (lane & 7) ^ swz_k128(row);
+    return (uint32_t)row * ld + (uint32_t)(lch << 4);
+  } else {
+    const int kr = 4 * wave + (lane >> 4), lch = (lane & 15) ^ swz_mn<16>(kr);
+    return mn0 + (lch << 4) < mn_lim ? (uint32_t)kr * ld + (uint32_t)(lch << 4) : kOOB;
+  }
+}
+template <bool KC>
+__device__ __forceinline__ uint32_t u128_step(uint32_t ld) { return KC ? 32u * ld : 16u * ld; }
+
+// K position inside its unit of the bytes load l of this lane brings in.
+template <bool KC, int NW>
+__device__ __forceinline__ int u128_kpos(int l, int wave, int lane) {
+  if constexpr (KC) return ((lane & 7) ^ swz_k128(8 * wave + (lane >> 3))) << 4;
+  else return 16 * l + 4 * wave + (lane >> 4);
+}
+
+template <int NW, bool A_KC, bool B_KC>
+struct UnitLoader {
+  static constexpr int SLOT = 256 * kKU;              // bytes of one slot
+  static constexpr int LPS = SLOT / 1024 / NW;        // loads per wave and load stage
+  static_assert(NW == 4, "the slot mapping assumes four waves");
+  int it = 0, j = 0, wg = 0, G = 1, units = 1;
+  uint32_t lslot = 0;          // slot of the next load stage
+  v4i ra, rb;
+  uint32_t a_base = 0, b_base = 0;
+  uint32_t a_tail = 0, b_tail = 0;    // bit l: load l lies past K in the tail unit
+
+  __device__ __forceinline__ void set_tile(const GemmKArgs& p, int v, int wave, int lane) {
+    int bt, tmi, tni;
+    map_tile(p, v, bt, tmi, tni);
+    const int m0 = tmi * 256, n0 = tni * 256;
+    const uint32_t a_tile_off = A_KC ? (uint32_t)m0 * p.lda : (uint32_t)m0;
+    const uint32_t b_tile_off = B_KC ? (uint32_t)n0 * p.ldb : (uint32_t)n0;
+    ra = rsrc_words(p.a + bt * p.stride_a + a_tile_off, p.extent_a - a_tile_off);
+    rb = rsrc_words(p.b + bt * p.stride_b + b_tile_off, p.extent_b - b_tile_off);
+    a_base = u128_base<A_KC, NW>(wave, lane, m0, p.m, p.lda);
+    b_base = u128_base<B_KC, NW>(wave, lane, n0, p.n, p.ldb);
+  }
+
+  __device__ __forceinline__ void init(const GemmKArgs& p, int wave, int lane, int wg_, int G_) {
+    wg = wg_;
+    G = G_;
+    units = (p.k + kKU - 1) / kKU;
+    const int kin = p.k % kKU;                        // K bytes of a partial last unit (0: none)
+#pragma unroll
+    for (int l = 0; l < LPS; ++l) {
+      a_tail |= (uint32_t)(kin != 0 && u128_kpos<A_KC, NW>(l, wave, lane) >= kin) << l;
+      b_tail |= (uint32_t)(kin != 0 && u128_kpos<B_KC, NW>(l, wave, lane) >= kin) << l;
+    }
+    set_tile(p, wg, wave, lane);
+  }
+
+  // Load l of the next load stage (operand OP: 0 = A, 1 = B).
+  template <int OP>
+  __device__ __forceinline__ void issue_one(const GemmKArgs& p, const lds_char_t* smem, int wave, int l) const {
+    const int u = j >> 1;
+    const bool tail = u == units - 1 && (p.k % kKU) != 0;
+    const uint32_t lds = lds_address(smem + lslot * SLOT) + (uint32_t)((l * NW + wave) * 1024);
+    constexpr bool KC = OP == 0 ? A_KC : B_KC;
+    const uint32_t ld = OP == 0 ? p.lda : p.ldb;
+    const uint32_t soff = KC ? (uint32_t)(u * kKU) : (uint32_t)(u * kKU) * ld;
+    const uint32_t voff = (OP == 0 ? a_base : b_base) + (uint32_t)l * u128_step<KC>(ld);
+    const bool oob = tail && (((OP == 0 ? a_tail : b_tail) >> l) & 1u);
+    load_lds16(OP == 0 ? ra : rb, lds, oob ? kOOB : voff, soff);
+  }
+
+  __device__ __forceinline__ void advance(const GemmKArgs& p, int my_tiles, int wave, int lane) {
+    lslot = lslot == kUSlots - 1 ? 0 : lslot + 1;
+    if (++j == 2 * units) {
+      j = 0;
+      if (++it < my_tiles) {
+        set_tile(p, wg + it * G, wave, lane);
+      } else {
+        ra[2] = 0;
+        rb[2] = 0;
+      }
+    }
+  }
+
+  template <int OP>
+  __device__ __forceinline__ void issue_stage(const GemmKArgs& p, const lds_char_t* smem, int my_tiles, int wave,
+                                              int lane) {
+#pragma unroll
+    for (int l = 0; l < LPS; ++l) issue_one<OP>(p, smem, wave, l);
+    advance(p, my_tiles, wave, lane);
+  }
+};
+
+// Zero the bytes at or past K of the chunk holding K's end in every row of the
+// K-contiguous slots of a partial last unit (one row per thread).
+template <bool A_KC, bool B_KC, int kThreads>
+__device__ __forceinline__ void zero_k_padding_u128(lds_char_t* slot_a, lds_char_t* slot_b, int k) {
+  const int kin = k % kKU;
+  const int c_lo = kin & ~15;
+  constexpr int ROWS = (A_KC ? 256 : 0) + (B_KC ? 256 : 0);
+  for (int r = threadIdx.x; r < ROWS; r += kThreads) {
+    const bool in_a = A_KC && r < 256;
+    const int row = in_a || !A_KC ? r : r - 256;
+    lds_char_t* rp = (in_a ? slot_a : slot_b) + row * kKU + (((c_lo >> 4) ^ swz_k128(row)) << 4) - c_lo;
+#pragma nounroll
+    for (int b = kin; b < c_lo + 16; ++b) rp[b] = 0;
+  }
+}
+
+template <bool A_KC, bool B_KC, int FA, int FB>
+__device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* smem, int wg, int G) {
+  constexpr int BM = 256, BN = 256, NW = 4, kThreads = 256;
+  constexpr int WM = 128, WN = 128, TM = 4, TN = 4, NM = TM * TN, NF = TM + TN;
+  constexpr int kFragMfmas = 3 * NM / 4;
+  using Loader = UnitLoader<NW, A_KC, B_KC>;
+  constexpr int SLOT = Loader::SLOT, LPS = Loader::LPS;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = (wave % 2) * WM, c0 = (wave / 2) * WN;
+  const int total = p.tiles_m * p.tiles_n * p.batch;
+  const int my_tiles = (total - 1 - wg) / G + 1;
+  const int units = (p.k + kKU - 1) / kKU;
+  const int kt_total = 2 * units;                    // half-stages per tile
+  const bool kfix = (p.k & 15) != 0;
+
+  const float sa_inv = p.a_scale_inv[0], sb_inv = p.b_scale_inv[0];
+  auto make_alpha = [&]() __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, sa_inv * sb_inv)));
+  };
+
+  v16f acc[TN][TM];
+  zero_acc(acc);
+  if (units == 0) {
+    const float alpha = make_alpha();
+    for (int it = 0; it < my_tiles; ++it)
+      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, nullptr);
+    return;
+  }
+
+  Loader ld;
+  ld.init(p, wave, lane, wg, G);
+  auto slot = [&](uint32_t i) __attribute__((always_inline)) { return smem + i * SLOT; };
+  uint32_t rslot = 0;          // A slot of the unit whose fragments are read next (its B: the next slot)
+  auto next_slot = [](uint32_t s) { return s == kUSlots - 1 ? 0u : s + 1; };
+  auto read_frags_u = [&](int h, v8i (&fa)[TM], v8i (&fb)[TN]) __attribute__((always_inline)) {
+    const lds_char_t* sa = slot(rslot);
+    const lds_char_t* sb = slot(next_slot(rslot));
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = frag_u128<A_KC>(sa, r0 + i * 32, lane, h);
+#pragma unroll
+    for (int i = 0; i < TN; ++i) fb[i] = frag_u128<B_KC>(sb, c0 + i * 32, lane, h);
+  };
+  // Zero the K padding of the unit about to be read when it is a partial
+  // last unit of a tile (the slots are visible: its loads have landed).
+  auto fix_tail_u = [&](bool last_unit) __attribute__((always_inline)) {
+    if (kfix && last_unit) {
+      zero_k_padding_u128<A_KC, B_KC, kThreads>(slot(rslot), slot(next_slot(rslot)), p.k);
+      lds_barrier();
+    }
+  };
+
+  v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+
+  // Half-stage t.  ODD: wait for the next unit, barrier, advance the read
+  // slot to it.  The MFMAs of fa / fb, each followed (READ) by its share of
+  // load stage t + 4 (operand A for even t, B for odd) and of the fragment
+  // reads of half-stage t + 1 (the same unit's second half for even t, the
+  // next unit's first half for odd t).
+  auto stage = [&](auto odd, auto read, bool next_last_unit, const v8i (&fa)[TM], const v8i (&fb)[TN],
+                   v8i (&na)[TM], v8i (&nb)[TN]) __attribute__((always_inline)) {
+    constexpr bool ODD = decltype(odd)::value, READ = decltype(read)::value;
+    constexpr int OP = ODD ? 1 : 0, H = ODD ? 0 : 1;
+    if constexpr (ODD) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+      lds_barrier();
+      rslot = next_slot(next_slot(rslot));
+      if (READ) fix_tail_u(next_last_unit);
+    }
+    const lds_char_t* sa = slot(rslot);
+    const lds_char_t* sb = slot(next_slot(rslot));
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int i = q / TM, j = q % TM;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+      if constexpr (READ) {
+#pragma unroll
+        for (int l = slot_items(q, NM, LPS, 0); l < slot_items(q + 1, NM, LPS, 0); ++l)
+          ld.template issue_one<OP>(p, smem, wave, l);
+        // Fragment reads only after the first three quarters of the MFMAs,
+        // so they have landed when the next half-stage starts.
+#pragma unroll
+        for (int f = slot_items(q, kFragMfmas, NF, 1); f < slot_items(q + 1, kFragMfmas, NF, 1); ++f) {
+          if (f < TM) na[f] = frag_u128<A_KC>(sa, r0 + f * 32, lane, H);
+          else nb[f - TM] = frag_u128<B_KC>(sb, c0 + (f - TM) * 32, lane, H);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if constexpr (READ) ld.advance(p, my_tiles, wave, lane);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // Prologue: load stages 0 .. 3 (units 0 and 1) in flight; unit 0 read.
+  ld.template issue_stage<0>(p, smem, my_tiles, wave, lane);
+  ld.template issue_stage<1>(p, smem, my_tiles, wave, lane);
+  ld.template issue_stage<0>(p, smem, my_tiles, wave, lane);
+  ld.template issue_stage<1>(p, smem, my_tiles, wave, lane);
+  const float alpha = make_alpha();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
+  lds_barrier();
+  fix_tail_u(units == 1);
+  read_frags_u(0, fa0, fb0);
+
+  for (int it = 0; it < my_tiles; ++it) {
+    int kt = 0;
+    for (; kt < kt_total - 2; kt += 2) {
+      stage(F{}, T{}, false, fa0, fb0, fa1, fb1);
+      stage(T{}, T{}, kt + 2 == kt_total - 2, fa1, fb1, fa0, fb0);
+    }
+    stage(F{}, T{}, false, fa0, fb0, fa1, fb1);
+    stage(T{}, F{}, false, fa1, fb1, fa0, fb0);
+    // The tile is stored through the slot its last half-stage's loads fill
+    // (held load stage t - 1, free since the barrier of that half-stage);
+    // then those loads go out, and the next tile's first fragments are read.
+    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, slot(ld.lslot));
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_zero_imm());
+    ld.template issue_stage<1>(p, smem, my_tiles, wave, lane);
+    zero_acc(acc);
+    fix_tail_u(units == 1 && it + 1 < my_tiles);
+    read_frags_u(0, fa0, fb0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
 // One problem per launch: workgroup blockIdx.x of gridDim.x.
 template <int BM, int BN, int WGM, int WGN, int NBUF, int OCC, bool A_KC, bool B_KC, int FA, int FB>
 __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, NBUF>()];
   gemm_body<BM, BN, WGM, WGN, NBUF, A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x,
                                                        (int)gridDim.x);
+}
+
+// The four-wave 256x256 tile on 128-byte load units (one problem per launch).
+template <bool A_KC, bool B_KC, int FA, int FB>
+__global__ __launch_bounds__(256, 1) void gemm_u128_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 256 * kKU];
+  gemm_body_u128<A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
 }
 
 // Two independent problems in one launch (a layer's dX and dW): workgroups
@@ -850,11 +1162,19 @@ GemmFn pick_fmt(int fa, int fb) {
 }
 
 template <bool AKC, bool BKC>
+GemmFn pick_u128(int fa, int fb) {
+  if (fa == 0 && fb == 0) return gemm_u128_kernel<AKC, BKC, 0, 0>;
+  if (fa == 1 && fb == 0) return gemm_u128_kernel<AKC, BKC, 1, 0>;
+  if (fa == 0 && fb == 1) return gemm_u128_kernel<AKC, BKC, 0, 1>;
+  return gemm_u128_kernel<AKC, BKC, 1, 1>;
+}
+
+template <bool AKC, bool BKC>
 GemmFn pick_large(int tile, int fa, int fb) {
   switch (tile) {
     case 5: return pick_fmt<256, 256, 2, 4, 4, 1, AKC, BKC>(fa, fb);
     case 6: return pick_fmt<256, 256, 4, 2, 4, 1, AKC, BKC>(fa, fb);
-    default: return pick_fmt<256, 256, 2, 2, 4, 1, AKC, BKC>(fa, fb);
+    default: return pick_u128<AKC, BKC>(fa, fb);
   }
 }
 
