@@ -284,6 +284,15 @@ __device__ __forceinline__ v4f bias4_full(const GemmKArgs& p, int n) {
 // 16-byte chunks are XOR-swizzled by row so the row-contiguous reads are free
 // of bank conflicts.  LDS operations of one wave run in order, so the reads
 // see the writes and later writes wait for earlier reads.
+// Global stores one wave issues in store_c_staged without a bias: TN * 32 /
+// CW column passes, each TM row bands of 32 rows read back in 16-byte chunks
+// (64 lanes cover 64 * 16 / (2 * CW) rows per store).
+template <int TM, int TN, int LPS>
+constexpr int staged_store_ops() {
+  constexpr int cw = staged_cols(TN * 32, LPS), rows_per_store = 64 * 16 / (2 * cw);
+  return (TN * 32 / cw) * TM * (32 / rows_per_store);
+}
+
 template <int BM, int BN, int TM, int TN, int NW, int LPS>
 __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&acc)[TN][TM], int m0, int n0,
                                                uint16_t* cb, int lane, int wave, float alpha, lds_char_t* buf) {
@@ -369,9 +378,14 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
 // consecutive columns (16 bytes) and each store instruction writes 32 rows x
 // 32 contiguous bytes.  Edge blocks go through the guarded path.  A bias load
 // makes the wave wait for the next tile's loads already in flight (the
-// compiler cannot count those), once per tile.
-template <int BM, int BN, int TM, int TN, int NW, int LPS>
-__device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
+// compiler cannot count those), once per tile.  Returns whether the block went through
+// LDS (then it issued exactly staged_store_ops<TM, TN, LPS>() global stores
+// and no other memory operation).  DRAIN: the guarded path ends by waiting
+// for all of the wave's vector memory operations, so a caller's loop finds
+// none of its loads pending (the compiler would otherwise wait for them, and
+// for every load in flight, at the loop's next register reuse).
+template <int BM, int BN, int TM, int TN, int NW, int LPS, bool DRAIN = false>
+__device__ __forceinline__ bool store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
                                              int lane, int wave, float alpha, lds_char_t* stage_buf) {
   int bt, tmi, tni;
   map_tile(p, v, bt, tmi, tni);
@@ -382,7 +396,7 @@ __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&ac
   if (stage_buf && (TM * TN <= 8 || p.bias_kind == 0) && p.ldc_small && m0 + TM * 32 <= p.m &&
       n0 + TN * 32 <= p.n) {
     store_c_staged<BM, BN, TM, TN, NW, LPS>(p, acc, m0, n0, cb, lane, wave, alpha, stage_buf);
-    return;
+    return true;
   }
   // (Blocks of more than 8 MFMA tiles keep their accumulators in AGPRs; for
   // them the fast path's extra registers cost more than it saves.)
@@ -412,7 +426,7 @@ __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&ac
         }
       }
     }
-    return;
+    return false;
   }
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
@@ -476,6 +490,8 @@ __device__ __forceinline__ void store_c_tile(const GemmKArgs& p, const v16f (&ac
       }
     }
   }
+  if constexpr (DRAIN) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  return false;
 }
 
 template <int TM, int TN>
@@ -840,8 +856,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 // The tile's half-stages come in pairs (even: A loads, reads the unit's second
 // half; odd: B loads, reads the next unit's first half), so the operand a
 // stage loads and the fragment sets are fixed at compile time.  K tails: a
-// unit past K loads zeros; the chunk holding K's end is zeroed past K in the
-// K-contiguous slots of a tile's last unit, as in the general kernel.
+// partial last unit loads whatever lies past K (bytes of the operand, or
+// zeros past its end) and, once landed, has its K positions past K zeroed in
+// LDS in both operands, so the loads carry no per-lane tail test.
 
 constexpr int kKU = 128;      // K bytes per load unit
 constexpr int kUSlots = 5;    // slots of the ring
@@ -893,13 +910,6 @@ __device__ __forceinline__ uint32_t u128_base(int wave, int lane, int mn0, int m
 template <bool KC>
 __device__ __forceinline__ uint32_t u128_step(uint32_t ld) { return KC ? 32u * ld : 16u * ld; }
 
-// K position inside its unit of the bytes load l of this lane brings in.
-template <bool KC, int NW>
-__device__ __forceinline__ int u128_kpos(int l, int wave, int lane) {
-  if constexpr (KC) return ((lane & 7) ^ swz_k128(8 * wave + (lane >> 3))) << 4;
-  else return 16 * l + 4 * wave + (lane >> 4);
-}
-
 template <int NW, bool A_KC, bool B_KC>
 struct UnitLoader {
   static constexpr int SLOT = 256 * kKU;              // bytes of one slot
@@ -909,7 +919,6 @@ struct UnitLoader {
   uint32_t lslot = 0;          // slot of the next load stage
   v4i ra, rb;
   uint32_t a_base = 0, b_base = 0;
-  uint32_t a_tail = 0, b_tail = 0;    // bit l: load l lies past K in the tail unit
 
   __device__ __forceinline__ void set_tile(const GemmKArgs& p, int v, int wave, int lane) {
     int bt, tmi, tni;
@@ -927,12 +936,6 @@ struct UnitLoader {
     wg = wg_;
     G = G_;
     units = (p.k + kKU - 1) / kKU;
-    const int kin = p.k % kKU;                        // K bytes of a partial last unit (0: none)
-#pragma unroll
-    for (int l = 0; l < LPS; ++l) {
-      a_tail |= (uint32_t)(kin != 0 && u128_kpos<A_KC, NW>(l, wave, lane) >= kin) << l;
-      b_tail |= (uint32_t)(kin != 0 && u128_kpos<B_KC, NW>(l, wave, lane) >= kin) << l;
-    }
     set_tile(p, wg, wave, lane);
   }
 
@@ -940,14 +943,12 @@ struct UnitLoader {
   template <int OP>
   __device__ __forceinline__ void issue_one(const GemmKArgs& p, const lds_char_t* smem, int wave, int l) const {
     const int u = j >> 1;
-    const bool tail = u == units - 1 && (p.k % kKU) != 0;
     const uint32_t lds = lds_address(smem + lslot * SLOT) + (uint32_t)((l * NW + wave) * 1024);
     constexpr bool KC = OP == 0 ? A_KC : B_KC;
     const uint32_t ld = OP == 0 ? p.lda : p.ldb;
     const uint32_t soff = KC ? (uint32_t)(u * kKU) : (uint32_t)(u * kKU) * ld;
     const uint32_t voff = (OP == 0 ? a_base : b_base) + (uint32_t)l * u128_step<KC>(ld);
-    const bool oob = tail && (((OP == 0 ? a_tail : b_tail) >> l) & 1u);
-    load_lds16(OP == 0 ? ra : rb, lds, oob ? kOOB : voff, soff);
+    load_lds16(OP == 0 ? ra : rb, lds, voff, soff);
   }
 
   __device__ __forceinline__ void advance(const GemmKArgs& p, int my_tiles, int wave, int lane) {
@@ -972,19 +973,26 @@ struct UnitLoader {
   }
 };
 
-// Zero the bytes at or past K of the chunk holding K's end in every row of the
-// K-contiguous slots of a partial last unit (one row per thread).
-template <bool A_KC, bool B_KC, int kThreads>
-__device__ __forceinline__ void zero_k_padding_u128(lds_char_t* slot_a, lds_char_t* slot_b, int k) {
-  const int kin = k % kKU;
-  const int c_lo = kin & ~15;
-  constexpr int ROWS = (A_KC ? 256 : 0) + (B_KC ? 256 : 0);
-  for (int r = threadIdx.x; r < ROWS; r += kThreads) {
-    const bool in_a = A_KC && r < 256;
-    const int row = in_a || !A_KC ? r : r - 256;
-    lds_char_t* rp = (in_a ? slot_a : slot_b) + row * kKU + (((c_lo >> 4) ^ swz_k128(row)) << 4) - c_lo;
+// Zero the K positions kin .. 127 (kin = K mod 128 > 0) of a tile's partial
+// last unit in one operand's slot, over whatever the loads brought there
+// (bytes of the operand past K, or zeros past its end): in a K-contiguous
+// slot bytes kin .. 127 of every row (chunk c of row r at c ^ swz_k128(r)),
+// in a crosswise slot the 256-byte k rows kin .. 127.
+template <bool KC, int kThreads>
+__device__ __forceinline__ void zero_k_tail_slot(lds_char_t* slot, int kin) {
+  const v4i z = v4i{0, 0, 0, 0};
+  if constexpr (KC) {
+    for (int r = threadIdx.x; r < 256; r += kThreads) {
+      lds_char_t* rp = slot + r * kKU;
+      const int sw = swz_k128(r);
 #pragma nounroll
-    for (int b = kin; b < c_lo + 16; ++b) rp[b] = 0;
+      for (int c = (kin + 15) >> 4; c < kKU / 16; ++c) *(lds_v4i_t*)(rp + ((c ^ sw) << 4)) = z;
+      lds_char_t* cp = rp + (((kin >> 4) ^ sw) << 4);
+#pragma nounroll
+      for (int b = kin & 15; b != 0 && b < 16; ++b) cp[b] = 0;
+    }
+  } else {
+    for (int i = threadIdx.x; i < (kKU - kin) * 16; i += kThreads) *(lds_v4i_t*)(slot + kin * 256 + i * 16) = z;
   }
 }
 
@@ -1003,7 +1011,9 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
   const int my_tiles = (total - 1 - wg) / G + 1;
   const int units = (p.k + kKU - 1) / kKU;
   const int kt_total = 2 * units;                    // half-stages per tile
-  const bool kfix = (p.k & 15) != 0;
+  const int kin = p.k % kKU;                         // K bytes of a partial last unit (0: none)
+  constexpr int kStoreOps = staged_store_ops<TM, TN, LPS>();
+  static_assert(LPS + kStoreOps <= 63, "vmcnt range");
 
   const float sa_inv = p.a_scale_inv[0], sb_inv = p.b_scale_inv[0];
   auto make_alpha = [&]() __attribute__((always_inline)) {
@@ -1035,28 +1045,35 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
   // Zero the K padding of the unit about to be read when it is a partial
   // last unit of a tile (the slots are visible: its loads have landed).
   auto fix_tail_u = [&](bool last_unit) __attribute__((always_inline)) {
-    if (kfix && last_unit) {
-      zero_k_padding_u128<A_KC, B_KC, kThreads>(slot(rslot), slot(next_slot(rslot)), p.k);
+    if (kin != 0 && last_unit) {
+      zero_k_tail_slot<A_KC, kThreads>(slot(rslot), kin);
+      zero_k_tail_slot<B_KC, kThreads>(slot(next_slot(rslot)), kin);
       lds_barrier();
     }
   };
+  // Set when the last epilogue stored through LDS: its kStoreOps stores sit
+  // between the load stages the next odd half-stage waits for and the one it
+  // leaves in flight.
+  bool after_store = false;
 
   v8i fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
   // Half-stage t.  ODD: wait for the next unit, barrier, advance the read
-  // slot to it.  The MFMAs of fa / fb, each followed (READ) by its share of
+  // slot to it.  The MFMAs of fa / fb, each followed by its share of
   // load stage t + 4 (operand A for even t, B for odd) and of the fragment
   // reads of half-stage t + 1 (the same unit's second half for even t, the
   // next unit's first half for odd t).
-  auto stage = [&](auto odd, auto read, bool next_last_unit, const v8i (&fa)[TM], const v8i (&fb)[TN],
+  auto stage = [&](auto odd, auto first, bool next_last_unit, const v8i (&fa)[TM], const v8i (&fb)[TN],
                    v8i (&na)[TM], v8i (&nb)[TN]) __attribute__((always_inline)) {
-    constexpr bool ODD = decltype(odd)::value, READ = decltype(read)::value;
+    constexpr bool ODD = decltype(odd)::value, FIRST = decltype(first)::value;
     constexpr int OP = ODD ? 1 : 0, H = ODD ? 0 : 1;
     if constexpr (ODD) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+      if (after_store) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS + kStoreOps));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
+      after_store = false;
       lds_barrier();
       rslot = next_slot(next_slot(rslot));
-      if (READ) fix_tail_u(next_last_unit);
+      fix_tail_u(next_last_unit);
     }
     const lds_char_t* sa = slot(rslot);
     const lds_char_t* sb = slot(next_slot(rslot));
@@ -1064,23 +1081,22 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
 #pragma unroll
     for (int q = 0; q < NM; ++q) {
       const int i = q / TM, j = q % TM;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], acc[i][j], FB, FA, 0, 0, 0, 0);
-      if constexpr (READ) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[i], fa[j], FIRST ? v16f{} : acc[i][j], FB,
+                                                                 FA, 0, 0, 0, 0);
 #pragma unroll
-        for (int l = slot_items(q, NM, LPS, 0); l < slot_items(q + 1, NM, LPS, 0); ++l)
-          ld.template issue_one<OP>(p, smem, wave, l);
-        // Fragment reads only after the first three quarters of the MFMAs,
-        // so they have landed when the next half-stage starts.
+      for (int l = slot_items(q, NM, LPS, 0); l < slot_items(q + 1, NM, LPS, 0); ++l)
+        ld.template issue_one<OP>(p, smem, wave, l);
+      // Fragment reads only after the first three quarters of the MFMAs, so
+      // they have landed when the next half-stage starts.
 #pragma unroll
-        for (int f = slot_items(q, kFragMfmas, NF, 1); f < slot_items(q + 1, kFragMfmas, NF, 1); ++f) {
-          if (f < TM) na[f] = frag_u128<A_KC>(sa, r0 + f * 32, lane, H);
-          else nb[f - TM] = frag_u128<B_KC>(sb, c0 + (f - TM) * 32, lane, H);
-        }
+      for (int f = slot_items(q, kFragMfmas, NF, 1); f < slot_items(q + 1, kFragMfmas, NF, 1); ++f) {
+        if (f < TM) na[f] = frag_u128<A_KC>(sa, r0 + f * 32, lane, H);
+        else nb[f - TM] = frag_u128<B_KC>(sb, c0 + (f - TM) * 32, lane, H);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    if constexpr (READ) ld.advance(p, my_tiles, wave, lane);
+    ld.advance(p, my_tiles, wave, lane);
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -1096,23 +1112,26 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
   fix_tail_u(units == 1);
   read_frags_u(0, fa0, fb0);
 
+  // The last half-stage of a tile loads and reads ahead into the next tile
+  // like any other (past the last tile its loads fetch nothing and its reads
+  // are never used).  A tile's first half-stage starts its accumulators from
+  // zero in the MFMAs themselves, so they carry nothing from tile to tile.
   for (int it = 0; it < my_tiles; ++it) {
-    int kt = 0;
-    for (; kt < kt_total - 2; kt += 2) {
-      stage(F{}, T{}, false, fa0, fb0, fa1, fb1);
-      stage(T{}, T{}, kt + 2 == kt_total - 2, fa1, fb1, fa0, fb0);
-    }
+    const bool next_tile_one_unit = units == 1 && it + 1 < my_tiles;
     stage(F{}, T{}, false, fa0, fb0, fa1, fb1);
-    stage(T{}, F{}, false, fa1, fb1, fa0, fb0);
-    // The tile is stored through the slot its last half-stage's loads fill
-    // (held load stage t - 1, free since the barrier of that half-stage);
-    // then those loads go out, and the next tile's first fragments are read.
-    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, slot(ld.lslot));
-    __builtin_amdgcn_s_waitcnt(lgkmcnt_zero_imm());
-    ld.template issue_stage<1>(p, smem, my_tiles, wave, lane);
-    zero_acc(acc);
-    fix_tail_u(units == 1 && it + 1 < my_tiles);
-    read_frags_u(0, fa0, fb0);
+    stage(T{}, F{}, units == 2 || next_tile_one_unit, fa1, fb1, fa0, fb0);
+    for (int kt = 2; kt < kt_total; kt += 2) {
+      stage(F{}, F{}, false, fa0, fb0, fa1, fb1);
+      stage(T{}, F{}, kt + 2 == kt_total - 2, fa1, fb1, fa0, fb0);   // (units > 1 here)
+    }
+    // The tile goes out through the slot of its last B, which the next
+    // half-stage's loads refill (free since the barrier of the last
+    // half-stage; each wave stages in the pieces its own loads fill, and its
+    // staging reads have returned before its stores issue).  The stores
+    // trail the loads the next odd half-stage waits for, and its wait lets
+    // them stay in flight.
+    after_store = store_c_tile<BM, BN, TM, TN, NW, LPS, true>(p, acc, wg + it * G, r0, c0, lane, wave, alpha,
+                                                              slot(ld.lslot));
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
