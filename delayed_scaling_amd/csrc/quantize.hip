@@ -32,9 +32,11 @@ namespace {
 constexpr int kQBlock = 256;     // threads per block
 constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
 constexpr int kDefaultBlocks = 1024;  // grid cap: 4 blocks per CU; larger inputs loop
+constexpr int k2dBlocks = 1024;       // grid cap of the transposed / dual quantize
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Element types.  mag() is a bit pattern of |x| that orders like |x| (NaN
@@ -92,21 +94,36 @@ __device__ __forceinline__ float clamp_fmax(float v) {
   return fminf(fmaxf(v, -m), m);
 }
 
-// Four elements (raw bits) to four codes packed in one word, NaN included:
-// a NaN element encodes as 0x7F with its sign.  amag collects max mag().
+// Four elements (raw bits) to four codes packed in one word; NaN elements
+// come out as whatever the convert makes of the clamped value (nan_fix4
+// repairs them).
+template <int FMT, int IN>
+__device__ __forceinline__ uint32_t cvt4(const uint32_t (&e)[4], float scale) {
+  using T = In<IN>;
+  const uint32_t out =
+      cvt_pair<FMT, false>(clamp_fmax<FMT>(T::f(e[0]) * scale), clamp_fmax<FMT>(T::f(e[1]) * scale), 0u);
+  return cvt_pair<FMT, true>(clamp_fmax<FMT>(T::f(e[2]) * scale), clamp_fmax<FMT>(T::f(e[3]) * scale), out);
+}
+
+// A NaN element encodes as 0x7F with its sign.
+template <int IN>
+__device__ __forceinline__ uint32_t nan_fix4(const uint32_t (&e)[4], uint32_t out) {
+  using T = In<IN>;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (T::mag(e[i]) > T::kInfMag) out = (out & ~(0xFFu << (8 * i))) | ((0x7Fu | T::sign(e[i])) << (8 * i));
+  return out;
+}
+
+// Four elements (raw bits) to four codes packed in one word, NaN included.
+// amag collects max mag().
 template <int FMT, int IN>
 __device__ __forceinline__ uint32_t quant4(const uint32_t (&e)[4], float scale, uint32_t& amag) {
   using T = In<IN>;
   const uint32_t m = max(max(T::mag(e[0]), T::mag(e[1])), max(T::mag(e[2]), T::mag(e[3])));
   amag = max(amag, m);
-  uint32_t out = cvt_pair<FMT, false>(clamp_fmax<FMT>(T::f(e[0]) * scale), clamp_fmax<FMT>(T::f(e[1]) * scale), 0u);
-  out = cvt_pair<FMT, true>(clamp_fmax<FMT>(T::f(e[2]) * scale), clamp_fmax<FMT>(T::f(e[3]) * scale), out);
-  if (m > T::kInfMag) {               // only chunks holding a NaN take this path
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (T::mag(e[i]) > T::kInfMag) out = (out & ~(0xFFu << (8 * i))) | ((0x7Fu | T::sign(e[i])) << (8 * i));
-  }
-  return out;
+  const uint32_t out = cvt4<FMT, IN>(e, scale);
+  return m > T::kInfMag ? nan_fix4<IN>(e, out) : out;
 }
 
 // 16 input bytes -> codes: 8 elements -> 2 words for 16-bit types, 4
@@ -121,6 +138,74 @@ __device__ __forceinline__ void quant16(v4u v, float scale, uint32_t (&out)[2], 
   } else {
     const uint32_t e[4] = {v.x, v.y, v.z, v.w};
     out[0] = quant4<FMT, IN>(e, scale, amag);
+  }
+}
+
+// Elements (raw bits) of 16 input bytes: 8 for 16-bit types (e[0..7]), 4 for
+// fp32 (e[0..3]).
+template <int IN>
+__device__ __forceinline__ void split16(v4u v, uint32_t (&e0)[4], uint32_t (&e1)[4]) {
+  if constexpr (In<IN>::kBits == 16) {
+    e0[0] = v.x & 0xFFFFu; e0[1] = v.x >> 16; e0[2] = v.y & 0xFFFFu; e0[3] = v.y >> 16;
+    e1[0] = v.z & 0xFFFFu; e1[1] = v.z >> 16; e1[2] = v.w & 0xFFFFu; e1[3] = v.w >> 16;
+  } else {
+    e0[0] = v.x; e0[1] = v.y; e0[2] = v.z; e0[3] = v.w;
+    e1[0] = e1[1] = e1[2] = e1[3] = 0u;
+  }
+}
+
+// Running max of mag() over whole 16-byte chunks.  16-bit types keep one
+// maximum per half-word (packed u16 max, one instruction per input word);
+// fp32 keeps one per word.
+template <int IN>
+struct MagMax {
+  uint32_t m = 0;   // two u16 maxima for 16-bit types, one u32 for fp32
+  __device__ __forceinline__ void add(v4u v) {
+    if constexpr (In<IN>::kBits == 16) {
+      u16x2 a = __builtin_bit_cast(u16x2, m);
+      a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu));
+      a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+      a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+      a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+      m = __builtin_bit_cast(uint32_t, a);
+    } else {
+      m = max(max(m, v.x & 0x7FFFFFFFu), max(v.y & 0x7FFFFFFFu, max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu)));
+    }
+  }
+  // The largest mag() seen, as one value.
+  __device__ __forceinline__ uint32_t get() const {
+    if constexpr (In<IN>::kBits == 16) return max(m & 0xFFFFu, m >> 16);
+    else return m;
+  }
+};
+
+// U whole 16-byte chunks to codes (o[u][0..1] for 16-bit types, o[u][0] for
+// fp32), NaN included, their max mag() folded into amag.  The NaN repair is
+// one wave-uniform test per group: it runs only when some lane's group holds
+// a NaN.
+template <int FMT, int IN, int U>
+__device__ __forceinline__ void quant_group(const v4u (&v)[U], float scale, uint32_t (&o)[U][2], uint32_t& amag) {
+  using T = In<IN>;
+  MagMax<IN> g;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    g.add(v[u]);
+    uint32_t e0[4], e1[4];
+    split16<IN>(v[u], e0, e1);
+    o[u][0] = cvt4<FMT, IN>(e0, scale);
+    o[u][1] = T::kBits == 16 ? cvt4<FMT, IN>(e1, scale) : 0u;
+  }
+  const uint32_t m = g.get();
+  amag = max(amag, m);
+  const bool nan = m > T::kInfMag;
+  if (__builtin_amdgcn_ballot_w64(nan) != 0 && nan) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t e0[4], e1[4];
+      split16<IN>(v[u], e0, e1);
+      o[u][0] = nan_fix4<IN>(e0, o[u][0]);
+      if constexpr (T::kBits == 16) o[u][1] = nan_fix4<IN>(e1, o[u][1]);
+    }
   }
 }
 
@@ -311,17 +396,13 @@ __device__ __forceinline__ void quantize_rows(const QuantJob& j, int G, int b, u
   const int64_t nchunk = j.nchunk;
   uint32_t amag = 0;
 
-  auto put = [&](int64_t c, const uint32_t (&o)[2], bool stream) __attribute__((always_inline)) {
-    if constexpr (kOut == 8) {
-      v2u* p = reinterpret_cast<v2u*>(y) + c;
-      const v2u w = {o[0], o[1]};
-      if (stream) __builtin_nontemporal_store(w, p);
-      else *p = w;
-    } else {
-      uint32_t* p = reinterpret_cast<uint32_t*>(y) + c;
-      if (stream) __builtin_nontemporal_store(o[0], p);
-      else *p = o[0];
-    }
+  // Streaming stores on every path (the compiler may merge the paths'
+  // stores; a plain store there measured 12 % slower on the whole pass).
+  auto put = [&](int64_t c, const uint32_t (&o)[2]) __attribute__((always_inline)) {
+    if constexpr (kOut == 8)
+      __builtin_nontemporal_store(v2u{o[0], o[1]}, reinterpret_cast<v2u*>(y) + c);
+    else
+      __builtin_nontemporal_store(o[0], reinterpret_cast<uint32_t*>(y) + c);
   };
   const int64_t step = (int64_t)G * kQBlock * kQUnroll;
   for (int64_t base = (int64_t)b * kQBlock * kQUnroll + threadIdx.x; base < nchunk; base += step) {
@@ -329,19 +410,17 @@ __device__ __forceinline__ void quantize_rows(const QuantJob& j, int G, int b, u
       v4u v[kQUnroll];
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) v[u] = __builtin_nontemporal_load(x + base + u * kQBlock);
+      uint32_t o[kQUnroll][2];
+      quant_group<FMT, IN, kQUnroll>(v, scale, o, amag);
 #pragma unroll
-      for (int u = 0; u < kQUnroll; ++u) {
-        uint32_t o[2];
-        quant16<FMT, IN>(v[u], scale, o, amag);
-        put(base + u * kQBlock, o, true);
-      }
+      for (int u = 0; u < kQUnroll; ++u) put(base + u * kQBlock, o[u]);
     } else {
       for (int u = 0; u < kQUnroll; ++u) {
         const int64_t c = base + u * kQBlock;
         if (c < nchunk) {
           uint32_t o[2];
           quant16<FMT, IN>(x[c], scale, o, amag);
-          put(c, o, false);
+          put(c, o);
         }
       }
     }
@@ -417,19 +496,32 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
   // whole 128-byte lines.
   constexpr int kPer = 16 / kElemBytes, kLoads = kTileC / kPer, kIters = kTileR * kLoads / kQBlock;
   constexpr int kWords = kPer / 4;                            // code words per load
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  // A tile's loads: piece j of this thread, zero outside x (cols % 16 == 0:
+  // a load is wholly in or out).
+  auto load_tile = [&](int t, v4u (&v)[kIters]) __attribute__((always_inline)) {
     const int r0 = (t / tiles_c) * kTileR, c0 = (t % tiles_c) * kTileC;
-    uint32_t w[kIters][2];
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
       const int item = threadIdx.x + j * kQBlock;
-      const int tr = item / kLoads, piece = item % kLoads;
-      const int r = r0 + tr, c = c0 + piece * kPer;
-      w[j][0] = w[j][1] = 0u;
-      if (r < rows && c < cols) {                            // cols % 16 == 0: whole load in or out
-        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes));
-        quant16<FMT, IN>(v, scale, w[j], amag);
-        if constexpr (DUAL) {
+      const int r = r0 + item / kLoads, c = c0 + (item % kLoads) * kPer;
+      v[j] = v4u{0u, 0u, 0u, 0u};
+      if (r < rows && c < cols)
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes));
+    }
+  };
+  // (Loading the next tile before this one's work measured slower.)
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int r0 = (t / tiles_c) * kTileR, c0 = (t % tiles_c) * kTileC;
+    v4u cur[kIters];
+    load_tile(t, cur);
+    uint32_t w[kIters][2];
+    quant_group<FMT, IN, kIters>(cur, scale, w, amag);
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int j = 0; j < kIters; ++j) {
+        const int item = threadIdx.x + j * kQBlock;
+        const int r = r0 + item / kLoads, c = c0 + (item % kLoads) * kPer;
+        if (r < rows && c < cols) {
           if constexpr (kWords == 2)
             __builtin_nontemporal_store(v2u{w[j][0], w[j][1]}, reinterpret_cast<v2u*>(y + (int64_t)r * cols + c));
           else
@@ -477,8 +569,9 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
       const int col = (threadIdx.x >> 3) + 32 * j, piece = threadIdx.x & 7;
       const int oc = c0 + col, orow = r0 + 16 * piece;
       const v4i v = *(const lds_v4i_t*)(ttile + col * kTStride + 16 * piece);
-      if (oc < cols && orow < rows)
-        *reinterpret_cast<v4i*>(y_t + (int64_t)oc * rows + orow) = v;
+      // (A plain store: streaming stores of the transposed output measured
+      // 7 % slower here.)
+      if (oc < cols && orow < rows) *reinterpret_cast<v4i*>(y_t + (int64_t)oc * rows + orow) = v;
     }
   }
 
@@ -570,19 +663,19 @@ constexpr int kGBf16 = 0, kGF16 = 1, kGF32 = 2, kGE4M3 = 3, kGE5M2 = 4;
 template <int GT>
 __device__ __forceinline__ void load8(const uint8_t* row, int col, float s_inv, float (&v)[8]) {
   if constexpr (GT == kGBf16 || GT == kGF16) {
-    const v4u w = *reinterpret_cast<const v4u*>(row + col * 2);
+    const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + col * 2));
     const uint32_t e[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
                            w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = GT == kGBf16 ? In<kInBf16>::f(e[i]) : In<kInF16>::f(e[i]);
   } else if constexpr (GT == kGF32) {
-    const v4u w0 = *reinterpret_cast<const v4u*>(row + col * 4);
-    const v4u w1 = *reinterpret_cast<const v4u*>(row + col * 4 + 16);
+    const v4u w0 = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + col * 4));
+    const v4u w1 = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + col * 4 + 16));
     const uint32_t e[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(e[i]);
   } else {
-    const v2u w = *reinterpret_cast<const v2u*>(row + col);
+    const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(row + col));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = (int)((i < 4 ? w.x : w.y) >> (8 * (i & 3)));
@@ -612,7 +705,20 @@ __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __res
   const int r_begin = slice * rows_per_slice;
   const int r_end = min(rows, r_begin + rows_per_slice);
   if (col < cols) {
-    for (int r = r_begin + rl; r < r_end; r += 32) {
+    // Rows r, r + 32, ... added in that order; eight rows' loads go out
+    // together.
+    constexpr int kRowsInFlight = 8;
+    int r = r_begin + rl;
+    for (; r + 32 * (kRowsInFlight - 1) < r_end; r += 32 * kRowsInFlight) {
+      float v[kRowsInFlight][8];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) load8<GT>(g + (int64_t)(r + 32 * u) * cols * kElem, col, s_inv, v[u]);
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
+    }
+    for (; r < r_end; r += 32) {
       float v[8];
       load8<GT>(g + (int64_t)r * cols * kElem, col, s_inv, v);
 #pragma unroll
@@ -791,7 +897,7 @@ int launch_quantize_2d(const void* x, int rows, int cols, int in_type, int fmt, 
   const int tiles_c = (cols + kTileC - 1) / kTileC;
   const int64_t ntiles = (int64_t)((rows + kTileR - 1) / kTileR) * tiles_c;
   int64_t blocks = ntiles < 1 ? 1 : ntiles;
-  if (max_blocks <= 0) max_blocks = kDefaultBlocks;
+  if (max_blocks <= 0) max_blocks = k2dBlocks;
   if (blocks > max_blocks) blocks = max_blocks;
   Quant2dFn fn = fmt == kE4M3 ? (dual ? quant2d_fn<kE4M3, true>(in_type) : quant2d_fn<kE4M3, false>(in_type))
                               : (dual ? quant2d_fn<kE5M2, true>(in_type) : quant2d_fn<kE5M2, false>(in_type));
