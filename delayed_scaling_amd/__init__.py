@@ -55,6 +55,13 @@ class _QuantJob(ctypes.Structure):
                 ("y", ctypes.c_void_p), ("scale_inv_out", ctypes.c_void_p)]
 
 
+# The same two structs as packed bytes (the calls pass them by address):
+# packing them is several times cheaper per call than filling the ctypes
+# structures, which document the layout and serve the ABI tests.
+_QJOB = struct.Struct("<QqQQQ")          # fp8_quantize_job, 40 bytes
+_MMARGS = struct.Struct("<3Q4i10q4Q")    # fp8_mm_args, 152 bytes
+
+
 class _MmArgs(ctypes.Structure):
     _fields_ = [
         ("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("c", ctypes.c_void_p),
@@ -87,19 +94,20 @@ def lib():
         L.fp8_quantize_with_grid.restype = ctypes.c_int
         L.fp8_quantize_with_grid.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        # Struct arguments travel as addresses: packed bytes or byref(ctypes struct).
         L.fp8_mm.restype = ctypes.c_int
-        L.fp8_mm.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_void_p]
+        L.fp8_mm.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         L.fp8_mm_with_tile.restype = ctypes.c_int
-        L.fp8_mm_with_tile.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_void_p]
+        L.fp8_mm_with_tile.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm_with_grid.restype = ctypes.c_int
-        L.fp8_mm_with_grid.argtypes = [ctypes.POINTER(_MmArgs), ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.fp8_mm_with_grid.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm_pair.restype = ctypes.c_int
-        L.fp8_mm_pair.argtypes = [ctypes.POINTER(_MmArgs), ctypes.POINTER(_MmArgs), ctypes.c_void_p]
+        L.fp8_mm_pair.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fp8_quantize_ex.restype = i32
         L.fp8_quantize_ex.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.fp8_quantize_batch.restype = i32
-        L.fp8_quantize_batch.argtypes = [ctypes.POINTER(_QuantJob), i32, i32, i32, vp]
+        L.fp8_quantize_batch.argtypes = [vp, i32, i32, i32, vp]
         L.fp8_quantize_2d.restype = i32
         L.fp8_quantize_2d.argtypes = [vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
         L.fp8_quantize_dynamic.restype = i32
@@ -122,15 +130,16 @@ def _check(status):
 
 
 def _stream(stream):
-    """The HIP stream to launch on: the given torch stream, else the current
-    stream of the current device (read without building a Stream object)."""
+    """The HIP stream to launch on (an address): the given torch stream, else
+    the current stream of the current device (read without building a Stream
+    object)."""
     if stream is None:
-        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
-    return ctypes.c_void_p(stream.cuda_stream)
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    return stream.cuda_stream
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _need(t, name, dtypes, nbytes, device=True):
@@ -189,10 +198,11 @@ class ScaleRing:
         self.hist_len, self.fmt = int(hist_len), int(fmt)
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
         scale_ring_init(self.buf, hist_len, fmt, init_scale, stream)
+        self._sinv = lib().fp8_ring_scale_inv(self.buf.data_ptr())
 
     def scale_inv_ptr(self):
         """Device address of scale_inv_used (what fp8_mm dequantizes with)."""
-        return lib().fp8_ring_scale_inv(ctypes.c_void_p(self.buf.data_ptr()))
+        return self._sinv
 
     def read(self):
         return read_ring(self.buf)
@@ -278,10 +288,8 @@ def fp8_quantize_batch(xs, fmt, rings, outs=None, scale_inv_outs=None, stream=No
     for i in range(n):
         if sio[i] is not None:
             _need(sio[i], f"scale_inv_outs[{i}]", _F32, 4)
-    jobs = (_QuantJob * n)()
-    for i in range(n):
-        jobs[i] = _QuantJob(xs[i].data_ptr(), xs[i].numel(), _ring_buf(rings[i]).data_ptr(), outs[i].data_ptr(),
-                            None if sio[i] is None else sio[i].data_ptr())
+    jobs = b"".join(_QJOB.pack(xs[i].data_ptr(), xs[i].numel(), _ring_buf(rings[i]).data_ptr(), outs[i].data_ptr(),
+                               0 if sio[i] is None else sio[i].data_ptr()) for i in range(n))
     _check(lib().fp8_quantize_batch(jobs, n, in_type, int(fmt), _stream(stream)))
     return outs
 
@@ -394,13 +402,20 @@ def fp8_bias_grad_noalloc(g, rows=None, cols=None, fmt=None, g_scale_inv=None, o
 
 
 def _addr(x):
+    """Device address of a tensor, a ScaleRing's scale_inv_used or an int
+    address; 0 for None."""
     if x is None:
-        return None
+        return 0
     if isinstance(x, int):
-        return ctypes.c_void_p(x)
+        return x
     if isinstance(x, ScaleRing):
-        return ctypes.c_void_p(x.scale_inv_ptr())
-    return ctypes.c_void_p(x.data_ptr())
+        return x._sinv
+    return x.data_ptr()
+
+
+def _extent(rows, cols, ld):
+    """Elements one stored [rows][cols] view with leading dimension ld spans."""
+    return (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
 
 
 def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=None, out=None,
@@ -422,14 +437,12 @@ def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias
     if out is None:
         out = torch.empty(nb * stride_c if nb > 1 else m * ldc, dtype=torch.bfloat16, device=dev)
     if m > 0 and n > 0:
-        # The extents the kernel touches, as the C side computes them: one
-        # batch entry of a stored [rows][cols] view spans (rows-1)*ld + cols
-        # elements; stride 0 broadcasts one entry.
-        ext = lambda rows, cols, ld: (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
+        # The extents the kernel touches, as the C side computes them
+        # (stride 0 broadcasts one entry).
         if k > 0:
-            _need(a, "a", _U8, (nb - 1) * stride_a + ext(a_rows, a_cols, lda), device=False)
-            _need(b, "b", _U8, (nb - 1) * stride_b + ext(b_rows, b_cols, ldb), device=False)
-        _need(out, "out", (torch.bfloat16,), 2 * ((nb - 1) * stride_c + ext(m, n, ldc)), device=False)
+            _need(a, "a", _U8, (nb - 1) * stride_a + _extent(a_rows, a_cols, lda), device=False)
+            _need(b, "b", _U8, (nb - 1) * stride_b + _extent(b_rows, b_cols, ldb), device=False)
+        _need(out, "out", (torch.bfloat16,), 2 * ((nb - 1) * stride_c + _extent(m, n, ldc)), device=False)
     bias_kind = BIAS_NONE
     if bias is not None:
         if bias.dtype == torch.uint8:
@@ -446,10 +459,10 @@ def _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias
             _need(sc, nm, _F32, 4, device=False)
     _on_device(("a", a), ("b", b), ("out", out), ("bias", bias), ("a_scale_inv", a_scale_inv),
                ("b_scale_inv", b_scale_inv), ("bias_scale_inv", bias_scale_inv))
-    args = _MmArgs(_addr(a), _addr(b), _addr(out), int(fmt_a), int(fmt_b), int(layout), bias_kind,
-                   int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
-                   int(stride_a), int(stride_b), int(stride_c),
-                   _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias), _addr(bias_scale_inv))
+    args = _MMARGS.pack(_addr(a), _addr(b), out.data_ptr(), int(fmt_a), int(fmt_b), int(layout), bias_kind,
+                        int(m), int(n), int(k), int(batch), int(lda), int(ldb), int(ldc),
+                        int(stride_a), int(stride_b), int(stride_c),
+                        _addr(a_scale_inv), _addr(b_scale_inv), _addr(bias), _addr(bias_scale_inv))
     return args, out
 
 
@@ -468,10 +481,10 @@ def fp8_mm(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias=N
     args, out = _mm_args(a, b, fmt_a, fmt_b, layout, m, n, k, a_scale_inv, b_scale_inv, bias, out, batch, lda,
                          ldb, ldc, stride_a, stride_b, stride_c, bias_fmt, bias_scale_inv)
     if tile is None and max_workgroups is None:
-        _check(lib().fp8_mm(ctypes.byref(args), _stream(stream)))
+        _check(lib().fp8_mm(args, _stream(stream)))
     else:
         t = -1 if tile is None else (TILES[tile] if isinstance(tile, str) else int(tile))
-        _check(lib().fp8_mm_with_grid(ctypes.byref(args), t, int(max_workgroups or 0), _stream(stream)))
+        _check(lib().fp8_mm_with_grid(args, t, int(max_workgroups or 0), _stream(stream)))
     return out
 
 
@@ -482,7 +495,7 @@ def fp8_mm_pair(first, second, stream=None):
     b_scale_inv and optionally bias, out, ...).  Returns the two outputs."""
     a0, out0 = _mm_args(**first)
     a1, out1 = _mm_args(**second)
-    _check(lib().fp8_mm_pair(ctypes.byref(a0), ctypes.byref(a1), _stream(stream)))
+    _check(lib().fp8_mm_pair(a0, a1, _stream(stream)))
     return out0, out1
 
 

@@ -200,14 +200,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// Wait until at most `stages` stages of LPS loads each are still in flight.
-template <int LPS, int STAGES>
-__device__ __forceinline__ void wait_stages(int stages) {
+// Wait until at most N stages of LPS loads each are still in flight.
+template <int LPS, int STAGES, int N>
+__device__ __forceinline__ void wait_stages() {
   static_assert(LPS * (STAGES - 1) <= 63, "vmcnt holds at most 63");
-  if (stages >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * LPS));
-  else if (stages == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPS));
-  else if (stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPS));
-  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  static_assert(N >= 0 && N < STAGES, "stages in flight");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N * LPS));
 }
 
 // Workgroup barrier ordering LDS only: outstanding global->LDS prefetches of
@@ -746,7 +744,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
     // Global loads after the even-numbered MFMAs, fragment reads after the
     // odd ones (a stage of one MFMA issues both after it).
     constexpr int LP = 0, FP = NM == 1 ? 0 : 1;
-    wait_stages<LPS, NBUF>(D - 2);
+    wait_stages<LPS, NBUF, D - 2>();
     stage_barrier();
     fix_tail(s, next_k);
     const typename Loader::Ctx c = ld.ctx(p, smem, wave, kt_full);
@@ -778,7 +776,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 #pragma unroll
   for (int st = 0; st < D; ++st) ld.issue_next(p, smem, my_tiles, kt_total, kt_full, wave, lane);
   const float alpha = make_alpha();
-  wait_stages<LPS, NBUF>(D - 1);
+  wait_stages<LPS, NBUF, D - 1>();
   lds_barrier();
   if (kfix && kt_full == 0) {
     zero_k_padding<BM, BN, A_KC, B_KC, kThreads>(buf(0), p.k, kt_full);

@@ -32,6 +32,7 @@ namespace {
 constexpr int kQBlock = 256;     // threads per block
 constexpr int kQUnroll = 4;      // 16-byte chunks in flight per thread
 constexpr int kDefaultBlocks = 1024;  // grid cap: 4 blocks per CU; larger inputs loop
+constexpr int kFlatTree = 64;         // launches of at most this many blocks skip the group level
 constexpr int k2dBlocks = 1024;       // grid cap of the transposed / dual quantize
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -246,6 +247,14 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
 // groups.  No release/acquire fence is needed: the only data handed between
 // blocks are the atomic words themselves.
 __device__ bool climb_tree(RingHeader* ring, uint32_t bmax, int G, int b) {
+  if (G <= kFlatTree) {
+    // Few blocks: every block goes straight to the top-level words.
+    const uint32_t prev = __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(prev);
+    const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_returned(t);
+    return t == (uint32_t)G - 1;
+  }
   const int ngroups = G < kRingGroups ? G : kRingGroups;
   const int g = b % kRingGroups;
   const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);

@@ -249,3 +249,22 @@ def test_binding_checks_tensors_before_the_call():
         ds.fp8_bias_grad(g, out=torch.empty(63, dtype=torch.bfloat16), workspace=u8(1 << 16))
     with pytest.raises(ds.Fp8dsError, match="workspace holds"):
         ds.fp8_bias_grad(g, out=torch.empty(64, dtype=torch.bfloat16), workspace=u8(16))
+
+
+def test_packed_structs_match_the_ctypes_layout():
+    """The binding packs fp8_mm_args and fp8_quantize_job with struct; the
+    bytes must equal the ctypes structures' (which spell out the header's
+    fields), field by field."""
+    vals = [0x1000, 0x2000, 0x3000, 1, 0, 2, 3, 17, 33, 65, 2, 80, 96, 112, 4096, 8192, 16384,
+            0x4000, 0x5000, 0x6000, 0x7000]
+    names = [f[0] for f in ds._MmArgs._fields_]
+    c = ds._MmArgs(*vals)
+    assert ds._MMARGS.size == ctypes.sizeof(ds._MmArgs)
+    assert ds._MMARGS.pack(*vals) == bytes(c)
+    for i, name in enumerate(names):           # one field at a time: no two fields swapped
+        one = [0] * len(vals)
+        one[i] = vals[i]
+        assert ds._MMARGS.pack(*one) == bytes(ds._MmArgs(**{name: vals[i]})), name
+    jv = [0x8000, 4096, 0x9000, 0xA000, 0xB000]
+    assert ds._QJOB.size == ctypes.sizeof(ds._QuantJob)
+    assert ds._QJOB.pack(*jv) == bytes(ds._QuantJob(*jv))
