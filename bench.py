@@ -50,19 +50,36 @@ def parse():
     ap.add_argument("--no-widened", action="store_true", help="skip the widened-path kernel timings")
     ap.add_argument("--no-linear-step", action="store_true", help="skip the 12-layer linear step")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-config timings")
+    ap.add_argument("--only-config", default=None,
+                    choices=["linear_d1024_t2048", "square_sweep", "skinny_batched", "chain_12_layers_t4096"],
+                    help="time one group of the per-config workloads only (nothing else) and print it")
     ap.add_argument("--settle-ms", type=float, default=400.0,
                     help="untimed steps after the warm-up, in milliseconds, before the timed steps")
     return ap.parse_args()
 
 
-def traffic_from_profile(kernel_src, sha_key, bytes_key):
+CSRC = os.path.join(ROOT, "delayed_scaling_amd", "csrc")
+# Device sources of each kernel family: the recorded HBM traffic holds only
+# while their hash is the one it was measured with.
+GEMM_SOURCES = [os.path.join(CSRC, f) for f in ("gemm_kernel.h", "gemm.hip", "device_common.h")]
+QUANT_SOURCES = [os.path.join(CSRC, f) for f in ("quantize.hip", "device_common.h")]
+
+
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(kernel_srcs, sha_key, bytes_key):
     """HBM bytes per launch recorded in profiles/ by the two PMC runs, or
-    None when the kernel source changed since they were taken."""
+    None when the kernel sources changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_8192_bench_kernels.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    sha = sources_sha(kernel_srcs)
     m_sha = re.search(rf"^{sha_key}:\s*([0-9a-f]{{64}})", text, re.M)
     m_b = re.search(rf"^{bytes_key}:\s*([0-9.eE+]+)", text, re.M)
     if not m_sha or not m_b or m_sha.group(1) != sha:
@@ -309,7 +326,7 @@ def gemm_entry(ms, m, n, k, batch, nbytes, workload):
             "flops": flops, "bytes": nbytes}
 
 
-def measure_configs(ds, stream):
+def measure_configs(ds, stream, only=None):
     """Every workload of the path besides the 8192^3 headline, each timed on
     its own (per-launch HIP events, median of 60-100 launches after warm-up)
     with inputs rotated over enough copies to exceed the 256 MB Infinity
@@ -363,35 +380,49 @@ def measure_configs(ds, stream):
                 "frac": round(gbps / PEAK_HBM_GBPS, 4), "roofline_us": round(3.0 * n / PEAK_HBM_GBPS / 1e3, 2),
                 "bytes": 3.0 * n}
 
+    def linear_layer():
+        return {
+            "gemm_fwd_nt": gemm("fwd", ds.NT, 2048, 4096, 1024, bias=True),
+            "gemm_dx_nn": gemm("dx", ds.NN, 2048, 1024, 4096, fa=1),
+            "gemm_dw_tn": gemm("dw", ds.TN, 4096, 1024, 2048, fa=1),
+            "quantize_x": quant("x", 2048, 1024, ds.E4M3, 1.0),
+            "quantize_w": quant("w", 4096, 1024, ds.E4M3, 1.0),
+            "quantize_g": quant("g", 2048, 4096, ds.E5M2, 1e-3),
+        }
+
+    def skinny_batched():
+        return {
+            "64x8192x2048": gemm("s1", ds.NT, 64, 8192, 2048),
+            "1024x1536x2048": gemm("s2", ds.NT, 1024, 1536, 2048),
+            "1024x1000x2048_bias": gemm("s3", ds.NT, 1024, 1000, 2048, bias=True),
+            "bmm_64x512x512x512": gemm("s4", ds.NT, 512, 512, 512, batch=64),
+            "bmm_8x1024x1024x2048_b_broadcast": gemm("s5", ds.NT, 1024, 1024, 2048, batch=8, bcast=True),
+        }
+
+    def chain():
+        c = measure_linear_step(stream, tokens=4096)
+        # Roofline of the chain: its GEMM FLOPs at the MFMA peak plus the bytes
+        # of its 144 quantizes (2 B read + 1 B written per element) at HBM peak.
+        dims = [(1024, 3072), (1024, 1024), (1024, 4096), (4096, 1024)] * 12
+        q_bytes = 3.0 * sum(4096 * i + o * i + 4096 * o for i, o in dims)
+        roof_ms = c["gemm_flops"] / (PEAK_FP8_TFLOPS * 1e12) * 1e3 + q_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
+        c["roofline_ms"] = round(roof_ms, 3)
+        c["frac"] = round(roof_ms / c["fp8_ms_per_step"], 4)
+        return c
+
     out = {}
-    out["linear_d1024_t2048"] = {
-        "gemm_fwd_nt": gemm("fwd", ds.NT, 2048, 4096, 1024, bias=True),
-        "gemm_dx_nn": gemm("dx", ds.NN, 2048, 1024, 4096, fa=1),
-        "gemm_dw_tn": gemm("dw", ds.TN, 4096, 1024, 2048, fa=1),
-        "quantize_x": quant("x", 2048, 1024, ds.E4M3, 1.0),
-        "quantize_w": quant("w", 4096, 1024, ds.E4M3, 1.0),
-        "quantize_g": quant("g", 2048, 4096, ds.E5M2, 1e-3),
-    }
-    torch.cuda.empty_cache()
-    out["square_sweep"] = {str(n): gemm(f"sq{n}", ds.NT, n, n, n) for n in (1024, 2048, 4096)}
-    torch.cuda.empty_cache()
-    out["skinny_batched"] = {
-        "64x8192x2048": gemm("s1", ds.NT, 64, 8192, 2048),
-        "1024x1536x2048": gemm("s2", ds.NT, 1024, 1536, 2048),
-        "1024x1000x2048_bias": gemm("s3", ds.NT, 1024, 1000, 2048, bias=True),
-        "bmm_64x512x512x512": gemm("s4", ds.NT, 512, 512, 512, batch=64),
-        "bmm_8x1024x1024x2048_b_broadcast": gemm("s5", ds.NT, 1024, 1024, 2048, batch=8, bcast=True),
-    }
-    torch.cuda.empty_cache()
-    chain = measure_linear_step(stream, tokens=4096)
-    # Roofline of the chain: its GEMM FLOPs at the MFMA peak plus the bytes of
-    # its 144 quantizes (2 B read + 1 B written per element) at HBM peak.
-    dims = [(1024, 3072), (1024, 1024), (1024, 4096), (4096, 1024)] * 12
-    q_bytes = 3.0 * sum(4096 * i + o * i + 4096 * o for i, o in dims)
-    roof_ms = chain["gemm_flops"] / (PEAK_FP8_TFLOPS * 1e12) * 1e3 + q_bytes / (PEAK_HBM_GBPS * 1e9) * 1e3
-    chain["roofline_ms"] = round(roof_ms, 3)
-    chain["frac"] = round(roof_ms / chain["fp8_ms_per_step"], 4)
-    out["chain_12_layers_t4096"] = chain
+    want = lambda name: only is None or only == name
+    if want("linear_d1024_t2048"):
+        out["linear_d1024_t2048"] = linear_layer()
+    if want("square_sweep"):
+        torch.cuda.empty_cache()
+        out["square_sweep"] = {str(n): gemm(f"sq{n}", ds.NT, n, n, n) for n in (1024, 2048, 4096)}
+    if want("skinny_batched"):
+        torch.cuda.empty_cache()
+        out["skinny_batched"] = skinny_batched()
+    if want("chain_12_layers_t4096"):
+        torch.cuda.empty_cache()
+        out["chain_12_layers_t4096"] = chain()
     return out
 
 
@@ -455,6 +486,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.only_config:
+        # One group of the per-config workloads and nothing else (to profile it).
+        print(json.dumps({"configs": measure_configs(ds, stream, only=args.only_config)}), flush=True)
+        return
 
     a_bits = bf16_normal((n, n), seed_for(3, 0, "A"))
     b_bits = bf16_normal((n, n), seed_for(3, 0, "B"))
@@ -525,10 +560,8 @@ def main():
     q_bytes = 6.0 * n * n       # two n x n bf16 tensors read, their codes written
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
-    traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip"),
-                                   "kernel_source_sha256", "hbm_bytes_per_launch")
-    q_traffic = traffic_from_profile(os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip"),
-                                     "quantize_source_sha256", "quantize_batch_hbm_bytes_per_launch")
+    traffic = traffic_from_profile(GEMM_SOURCES, "kernel_source_sha256", "hbm_bytes_per_launch")
+    q_traffic = traffic_from_profile(QUANT_SOURCES, "quantize_source_sha256", "quantize_batch_hbm_bytes_per_launch")
 
     out = {
         "metric": "FP8 GEMM TFLOP/s (E4M3 NT 8192^3) + quantize GB/s, % of MI355X peak",
@@ -548,7 +581,8 @@ def main():
                    "m": n, "n": n, "k": n, "hist_len": 16, "input_rotation": rot},
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "gemm_kernel 256x256 tile, 4 waves, NT, E4M3 x E4M3",
+                     "traffic": traffic,
+                     "kernel": "gemm_u128_kernel<NT, E4M3 x E4M3>: 256x256 tile, 4 waves, 128-byte K units",
                      "avg_launch_us": round(g_avg * 1e3, 2), "launch_us": spread(g_ms)},
         "clock_settle": {"ms": round(settle_ms, 1), "steps": settle_steps,
                          "note": "untimed steps after the warm-up steps, before the timed ones"},
@@ -565,8 +599,7 @@ def main():
         out["widened"] = measure_widened(ds, n, stream)
         if not args.no_linear_step:
             out["widened"]["linear_step_12_layers"] = measure_linear_step(stream)
-        qsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "quantize.hip")
-        gsrc = os.path.join(ROOT, "delayed_scaling_amd", "csrc", "gemm.hip")
+        qsrc, gsrc = QUANT_SOURCES, GEMM_SOURCES
         for name, entry in out["widened"].items():
             if "bound" not in entry:
                 continue

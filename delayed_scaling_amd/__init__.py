@@ -198,7 +198,8 @@ class ScaleRing:
         self.hist_len, self.fmt = int(hist_len), int(fmt)
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
         scale_ring_init(self.buf, hist_len, fmt, init_scale, stream)
-        self._sinv = lib().fp8_ring_scale_inv(self.buf.data_ptr())
+        self._bufp = self.buf.data_ptr()
+        self._sinv = lib().fp8_ring_scale_inv(self._bufp)
 
     def scale_inv_ptr(self):
         """Device address of scale_inv_used (what fp8_mm dequantizes with)."""

@@ -14,11 +14,16 @@ quantized in one batched launch that also writes both applied 1/scale values
 into a small tensor the backward keeps.  Every arithmetic step runs in the
 library's kernels; this module only allocates outputs and orders the calls
 on the current stream.
+
+The layer calls the C ABI directly with packed argument structs: every
+buffer but x, w, b and the incoming gradient is one it allocated itself with
+the size the call needs, so the per-tensor checks of the general binding
+(which cost more host time than the launches) reduce to those four tensors.
 """
 import torch
 
-from . import (E4M3, E5M2, NN, NT, TN, BiasGradWorkspace, ScaleRing, bias_grad_workspace_bytes, fp8_bias_grad,
-               fp8_mm, fp8_mm_pair, fp8_quantize, fp8_quantize_batch)
+from . import (_IN_TYPE, _MMARGS, _QJOB, BIAS_BF16, BIAS_F32, BIAS_NONE, E4M3, E5M2, G_BF16, NN, NT, TN,
+               BiasGradWorkspace, Fp8dsError, ScaleRing, _check, _stream, bias_grad_workspace_bytes, lib)
 
 
 class Fp8LinearState:
@@ -30,11 +35,36 @@ class Fp8LinearState:
         self.ring_w = ScaleRing(hist_len, E4M3, device=device)
         self.ring_g = ScaleRing(hist_len, E5M2, device=device)
         self.workspace = None
+        self._ws_shape = None
 
     def bias_workspace(self, rows, cols, device):
-        if self.workspace is None or self.workspace.buf.numel() < bias_grad_workspace_bytes(rows, cols):
-            self.workspace = BiasGradWorkspace(rows, cols, device)
+        if self._ws_shape != (rows, cols):
+            if self.workspace is None or self.workspace.buf.numel() < bias_grad_workspace_bytes(rows, cols):
+                self.workspace = BiasGradWorkspace(rows, cols, device)
+            self._ws_shape = (rows, cols)
         return self.workspace
+
+
+def _input(t, name, dev):
+    """A caller's tensor going to a kernel: bf16 / fp16 / fp32, on the GPU of
+    the layer, made contiguous."""
+    if t.dtype not in _IN_TYPE:
+        raise Fp8dsError(f"{name} must be bf16, fp16 or fp32, not {t.dtype}")
+    if t.device != dev:
+        raise Fp8dsError(f"{name} is on {t.device}; the layer runs on {dev}")
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _mm(a, b, c, fmt_a, layout, m, n, k, sa, sb, bias=None, bias_kind=BIAS_NONE):
+    """The argument struct of one dense GEMM (formats fmt_a x E4M3) over
+    contiguous operands the layer allocated."""
+    a_cols = m if layout == TN else k
+    b_cols = k if layout == NT else n
+    a_rows = k if layout == TN else m
+    b_rows = n if layout == NT else k
+    return _MMARGS.pack(a.data_ptr(), b.data_ptr(), c.data_ptr(), fmt_a, E4M3, layout, bias_kind, m, n, k, 1,
+                        a_cols, b_cols, n, a_rows * a_cols, b_rows * b_cols, m * n, sa, sb,
+                        0 if bias is None else bias.data_ptr(), 0)
 
 
 class _Fp8LinearFn(torch.autograd.Function):
@@ -42,18 +72,33 @@ class _Fp8LinearFn(torch.autograd.Function):
     def forward(ctx, x, w, b, state):
         n_in = x.shape[-1]
         n_out = w.shape[0]
-        x2 = x.reshape(-1, n_in).contiguous()
-        w2 = w.contiguous()
+        if w.dim() != 2 or w.shape[1] != n_in:
+            raise Fp8dsError(f"weight {tuple(w.shape)} does not take inputs of {n_in} features")
+        dev = w.device
+        x2 = _input(x.reshape(-1, n_in), "x", dev)
+        w2 = _input(w, "weight", dev)
         t = x2.shape[0]
-        s = torch.empty(2, dtype=torch.float32, device=x.device)   # applied 1/scale of X and W
-        sx, sw = s[0:1], s[1:2]
+        L, st = lib(), _stream(None)
+        s = torch.empty(2, dtype=torch.float32, device=dev)   # applied 1/scale of X and W
+        sp = s.data_ptr()
+        x8 = torch.empty((t, n_in), dtype=torch.uint8, device=dev)
+        w8 = torch.empty((n_out, n_in), dtype=torch.uint8, device=dev)
+        jx = _QJOB.pack(x2.data_ptr(), x2.numel(), state.ring_x._bufp, x8.data_ptr(), sp)
+        jw = _QJOB.pack(w2.data_ptr(), w2.numel(), state.ring_w._bufp, w8.data_ptr(), sp + 4)
         if x2.dtype == w2.dtype:
-            x8, w8 = fp8_quantize_batch([x2, w2], E4M3, [state.ring_x, state.ring_w], scale_inv_outs=[sx, sw])
+            _check(L.fp8_quantize_batch(jx + jw, 2, _IN_TYPE[x2.dtype], E4M3, st))
         else:
-            x8, = fp8_quantize_batch([x2], E4M3, [state.ring_x], scale_inv_outs=[sx])
-            w8, = fp8_quantize_batch([w2], E4M3, [state.ring_w], scale_inv_outs=[sw])
-        y = fp8_mm(x8, w8, E4M3, E4M3, NT, t, n_out, n_in, sx, sw, bias=b)
-        ctx.save_for_backward(x8, w8, sx, sw)
+            _check(L.fp8_quantize_batch(jx, 1, _IN_TYPE[x2.dtype], E4M3, st))
+            _check(L.fp8_quantize_batch(jw, 1, _IN_TYPE[w2.dtype], E4M3, st))
+        bias_kind = BIAS_NONE
+        if b is not None:
+            bias_kind = {torch.bfloat16: BIAS_BF16, torch.float32: BIAS_F32}.get(b.dtype)
+            if bias_kind is None or b.device != dev or b.numel() != n_out:
+                raise Fp8dsError("bias must be a bf16 or fp32 tensor of out_features elements on the layer's GPU")
+            b = b if b.is_contiguous() else b.contiguous()
+        y = torch.empty((t, n_out), dtype=torch.bfloat16, device=dev)
+        _check(L.fp8_mm(_mm(x8, w8, y, E4M3, NT, t, n_out, n_in, sp, sp + 4, b, bias_kind), st))
+        ctx.save_for_backward(x8, w8, s)
         ctx.state = state
         ctx.dims = (t, n_in, n_out)
         ctx.x_shape = x.shape
@@ -62,25 +107,38 @@ class _Fp8LinearFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, gy):
-        x8, w8, sx, sw = ctx.saved_tensors
+        x8, w8, s = ctx.saved_tensors
         t, n_in, n_out = ctx.dims
         state = ctx.state
-        g2 = gy.reshape(-1, n_out).to(torch.bfloat16).contiguous()
-        g8 = fp8_quantize(g2, E5M2, state.ring_g)
+        dev = x8.device
+        g2 = gy.reshape(-1, n_out)
+        if g2.dtype != torch.bfloat16 or not g2.is_contiguous():
+            g2 = g2.to(torch.bfloat16).contiguous()
+        L, st = lib(), _stream(None)
+        sp = s.data_ptr()
+        g8 = torch.empty((t, n_out), dtype=torch.uint8, device=dev)
+        _check(L.fp8_quantize(g2.data_ptr(), g2.numel(), E5M2, state.ring_g._bufp, g8.data_ptr(), st))
+        sg = state.ring_g._sinv
         dx = dw = db = None
-        dx_args = dict(a=g8, b=w8, fmt_a=E5M2, fmt_b=E4M3, layout=NN, m=t, n=n_in, k=n_out,
-                       a_scale_inv=state.ring_g, b_scale_inv=sw)
-        dw_args = dict(a=g8, b=x8, fmt_a=E5M2, fmt_b=E4M3, layout=TN, m=n_out, n=n_in, k=t,
-                       a_scale_inv=state.ring_g, b_scale_inv=sx)
-        if ctx.needs_input_grad[0] and ctx.needs_input_grad[1]:
-            dx, dw = fp8_mm_pair(dx_args, dw_args)           # one launch for both
-            dx, dw = dx.view(ctx.x_shape), dw.view(n_out, n_in)
-        elif ctx.needs_input_grad[0]:
-            dx = fp8_mm(**dx_args).view(ctx.x_shape)
-        elif ctx.needs_input_grad[1]:
-            dw = fp8_mm(**dw_args).view(n_out, n_in)
+        need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_x:
+            dx = torch.empty((t, n_in), dtype=torch.bfloat16, device=dev)
+            ax = _mm(g8, w8, dx, E5M2, NN, t, n_in, n_out, sg, sp + 4)
+        if need_w:
+            dw = torch.empty((n_out, n_in), dtype=torch.bfloat16, device=dev)
+            aw = _mm(g8, x8, dw, E5M2, TN, n_out, n_in, t, sg, sp)
+        if need_x and need_w:
+            _check(L.fp8_mm_pair(ax, aw, st))                   # one launch for both
+        elif need_x:
+            _check(L.fp8_mm(ax, st))
+        elif need_w:
+            _check(L.fp8_mm(aw, st))
+        if dx is not None:
+            dx = dx.view(ctx.x_shape)
         if ctx.has_bias and ctx.needs_input_grad[2]:
-            db = fp8_bias_grad(g2, t, n_out, workspace=state.bias_workspace(t, n_out, g2.device))
+            ws = state.bias_workspace(t, n_out, dev)
+            db = torch.empty(n_out, dtype=torch.bfloat16, device=dev)
+            _check(L.fp8_bias_grad(g2.data_ptr(), t, n_out, G_BF16, None, 0, db.data_ptr(), ws.buf.data_ptr(), st))
         return dx, dw, db, None
 
 
