@@ -468,20 +468,28 @@ __global__ __launch_bounds__(kQBlock) void quantize_batch_kernel(QuantBatch batc
 
 // ---------------------------------------------------------------------------
 // Transposed / dual quantize of an R x C row-major tensor, R and C multiples
-// of 16.  A block takes a 128-row x 64-column tile:
+// of 16.  A block takes a 128-row x 128-column tile:
 //  1. threads quantize 16-byte pieces of the tile's rows, consecutive threads
 //     on consecutive pieces (and, for the dual form, store those codes), and
-//     write the codes to an LDS tile [128 rows][64 codes] whose 16-byte chunks
-//     are XOR-swizzled per row;
-//  2. transpose reads (ds_read_b64_tr_b8) hand each lane 32 consecutive rows
-//     of one column, which it writes to a second LDS tile [64 columns][128
+//     write the codes to an LDS tile [128 rows][128 codes] whose 16-byte
+//     chunks are XOR-swizzled per row;
+//  2. transpose reads (ds_read_b64_tr_b8) hand each lane 64 consecutive rows
+//     of one column, which it writes to a second LDS tile [128 columns][128
 //     rows] (rows padded to 144 bytes against bank conflicts);
 //  3. eight lanes per column then store 16 bytes each: every store
 //     instruction writes whole 128-byte lines of the transposed output.
+// Each tile row reads 256 contiguous input bytes (bf16): on this part the
+// mix of row reads and transposed 128-byte writes measured 6-10 % faster
+// with 256-byte than with 128-byte read segments (a probe that only moves
+// the bytes), and the 64-column tile of the first version left the kernel
+// at 0.56 of the HBM nameplate.
 
-constexpr int kTileR = 128, kTileC = 64, kTStride = kTileR + 16;
+constexpr int kTileR = 128, kTileC = 128, kTStride = kTileR + 16;
 
-__device__ __forceinline__ int tile_swz(int r) { return ((r >> 2) & 1) << 1; }
+// Chunk c of codes-tile row r sits at c ^ tile_swz(r): the 8 rows of a
+// transpose read (one 16-byte chunk each, 128-byte rows) then fall on 8
+// distinct 16-byte bank slots.
+__device__ __forceinline__ int tile_swz(int r) { return (r >> 1) & 7; }
 
 template <int FMT, int IN, bool DUAL>
 __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __restrict__ x, uint8_t* __restrict__ y,
@@ -505,24 +513,17 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
   // whole 128-byte lines.
   constexpr int kPer = 16 / kElemBytes, kLoads = kTileC / kPer, kIters = kTileR * kLoads / kQBlock;
   constexpr int kWords = kPer / 4;                            // code words per load
-  // A tile's loads: piece j of this thread, zero outside x (cols % 16 == 0:
-  // a load is wholly in or out).
-  auto load_tile = [&](int t, v4u (&v)[kIters]) __attribute__((always_inline)) {
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int r0 = (t / tiles_c) * kTileR, c0 = (t % tiles_c) * kTileC;
+    v4u cur[kIters];
 #pragma unroll
     for (int j = 0; j < kIters; ++j) {
       const int item = threadIdx.x + j * kQBlock;
       const int r = r0 + item / kLoads, c = c0 + (item % kLoads) * kPer;
-      v[j] = v4u{0u, 0u, 0u, 0u};
+      cur[j] = v4u{0u, 0u, 0u, 0u};                          // cols % 16 == 0: a load is wholly in or out
       if (r < rows && c < cols)
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes));
+        cur[j] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(x + ((int64_t)r * cols + c) * kElemBytes));
     }
-  };
-  // (Loading the next tile before this one's work measured slower.)
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int r0 = (t / tiles_c) * kTileR, c0 = (t % tiles_c) * kTileC;
-    v4u cur[kIters];
-    load_tile(t, cur);
     uint32_t w[kIters][2];
     quant_group<FMT, IN, kIters>(cur, scale, w, amag);
     if constexpr (DUAL) {
@@ -550,36 +551,36 @@ __global__ __launch_bounds__(kQBlock) void quantize_2d_kernel(const uint8_t* __r
     }
     __syncthreads();
     {
-      // Lane l of wave w takes column 32*(w&1) + l%32 and tile rows
-      // 64*(w>>1) + 32*(l/32) + [0, 32).  Within each 16-lane group, the even
-      // lanes address rows k..k+7 of the group's first 8 columns and the odd
-      // lanes the next 8; each read hands a lane 8 consecutive rows of its
+      // Lane l of wave w takes column 32*w + l%32 and tile rows 64*(l/32) +
+      // [0, 64).  Within each 16-lane group, the even lanes address rows
+      // k..k+7 of the group's 16-column chunk and the odd lanes the other 8
+      // bytes of those rows; each read hands a lane 8 consecutive rows of its
       // column.
-      const int col = 32 * (wave & 1) + (lane & 31);
-      const int rbase = 64 * (wave >> 1) + 32 * (lane >> 5);
+      const int col = 32 * wave + (lane & 31);
+      const int rbase = 64 * (lane >> 5);
       const int q = lane & 15;
-      const int chunk = 2 * (wave & 1) + ((lane >> 4) & 1);
-      v2i part[4];
+      const int chunk = 2 * wave + ((lane >> 4) & 1);
+      v2i part[8];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
+      for (int h = 0; h < 8; ++h) {
         const int kr = rbase + 8 * h + (q >> 1);
         const int addr = kr * kTileC + ((chunk ^ tile_swz(kr)) << 4) + 8 * (q & 1);
         part[h] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i_t*)(tile + addr));
       }
       lds_char_t* dst = ttile + col * kTStride + rbase;
-      *(lds_v4i_t*)dst = v4i{part[0][0], part[0][1], part[1][0], part[1][1]};
-      *(lds_v4i_t*)(dst + 16) = v4i{part[2][0], part[2][1], part[3][0], part[3][1]};
+#pragma unroll
+      for (int h = 0; h < 8; h += 2)
+        *(lds_v4i_t*)(dst + 8 * h) = v4i{part[h][0], part[h][1], part[h + 1][0], part[h + 1][1]};
     }
     __syncthreads();
     // Eight lanes per column, 16 bytes each: column t/8 + 32*j, rows
-    // 16*(t%8) + [0, 16) of the tile.
+    // 16*(t%8) + [0, 16) of the tile.  (A plain store: streaming stores of
+    // the transposed output measured 7 % slower here.)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kTileC / 32; ++j) {
       const int col = (threadIdx.x >> 3) + 32 * j, piece = threadIdx.x & 7;
       const int oc = c0 + col, orow = r0 + 16 * piece;
       const v4i v = *(const lds_v4i_t*)(ttile + col * kTStride + 16 * piece);
-      // (A plain store: streaming stores of the transposed output measured
-      // 7 % slower here.)
       if (oc < cols && orow < rows) *reinterpret_cast<v4i*>(y_t + (int64_t)oc * rows + orow) = v;
     }
   }
