@@ -655,10 +655,11 @@ __global__ __launch_bounds__(kQBlock) void amax_kernel(const v4u* __restrict__ x
 
 // ---------------------------------------------------------------------------
 // Bias gradient: out[c] = sum_r g[r][c] in fp32, g bf16 / fp16 / fp32 or 8-bit
-// codes dequantized as dec(code) * s_inv.  A block takes 64 columns and a
-// slice of the rows; thread t sums columns 8*(t%8) .. +7 over rows t/8,
-// t/8 + 32, ... of its slice, the 32 row lanes are added in a fixed order in
-// LDS, and the slice's 64 sums go to the workspace.  Consecutive blocks take
+// codes dequantized as dec(code) * s_inv.  A block takes 128 columns (256
+// bytes of a bf16 row: 128-byte row pieces measured 8 % slower) and a slice
+// of the rows; thread t sums columns 8*(t%16) .. +7 over rows t/16,
+// t/16 + 16, ... of its slice, the 16 row lanes are added in a fixed order in
+// LDS, and the slice's 128 sums go to the workspace.  Consecutive blocks take
 // consecutive strips of one slice, so the blocks running together read whole
 // rows.  The last block of a column strip (a ticket per strip, as in the
 // ring's completion tree) adds the slices in order, its loads of them issued
@@ -695,7 +696,9 @@ __device__ __forceinline__ void load8(const uint8_t* row, int col, float s_inv, 
   }
 }
 
-constexpr int kGradCols = 64;
+constexpr int kGradCols = 128;                      // columns per strip (256 bytes of a bf16 row)
+constexpr int kGradGroups = kGradCols / 8;          // 8-column groups, one per thread of a row lane
+constexpr int kGradRowLanes = kQBlock / kGradGroups;
 
 template <int GT>
 __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __restrict__ g, int rows, int cols,
@@ -704,31 +707,31 @@ __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __res
                                                             void* __restrict__ out, float* __restrict__ partial,
                                                             uint32_t* __restrict__ tickets) {
   constexpr int kElem = GT == kGF32 ? 4 : (GT == kGBf16 || GT == kGF16) ? 2 : 1;
-  __shared__ float sums[32][kGradCols + 1];
+  __shared__ float sums[kGradRowLanes][kGradCols + 1];
   __shared__ int s_last;
   const int strips = (int)gridDim.x / slices, strip = blockIdx.x % strips, slice = blockIdx.x / strips;
   const int c0 = strip * kGradCols;
-  const int cg = threadIdx.x & 7, rl = threadIdx.x >> 3;   // 8-column group, row lane
+  const int cg = threadIdx.x % kGradGroups, rl = threadIdx.x / kGradGroups;   // 8-column group, row lane
   const int col = c0 + 8 * cg;
   const float s_inv = (GT == kGE4M3 || GT == kGE5M2) ? g_scale_inv[0] : 1.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int r_begin = slice * rows_per_slice;
   const int r_end = min(rows, r_begin + rows_per_slice);
   if (col < cols) {
-    // Rows r, r + 32, ... added in that order; eight rows' loads go out
-    // together.
-    constexpr int kRowsInFlight = 8;
+    // Rows r, r + kGradRowLanes, ... added in that order; eight rows' loads
+    // go out together.
+    constexpr int kRowsInFlight = 8, kStep = kGradRowLanes;
     int r = r_begin + rl;
-    for (; r + 32 * (kRowsInFlight - 1) < r_end; r += 32 * kRowsInFlight) {
+    for (; r + kStep * (kRowsInFlight - 1) < r_end; r += kStep * kRowsInFlight) {
       float v[kRowsInFlight][8];
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) load8<GT>(g + (int64_t)(r + 32 * u) * cols * kElem, col, s_inv, v[u]);
+      for (int u = 0; u < kRowsInFlight; ++u) load8<GT>(g + (int64_t)(r + kStep * u) * cols * kElem, col, s_inv, v[u]);
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] += v[u][i];
     }
-    for (; r < r_end; r += 32) {
+    for (; r < r_end; r += kStep) {
       float v[8];
       load8<GT>(g + (int64_t)r * cols * kElem, col, s_inv, v);
 #pragma unroll
@@ -740,7 +743,7 @@ __global__ __launch_bounds__(kQBlock) void bias_grad_kernel(const uint8_t* __res
   __syncthreads();
   if (threadIdx.x < kGradCols) {
     float s = 0.f;
-    for (int j = 0; j < 32; ++j) s += sums[j][threadIdx.x];
+    for (int j = 0; j < kGradRowLanes; ++j) s += sums[j][threadIdx.x];
     if (c0 + threadIdx.x < cols)
       __hip_atomic_store(partial + (int64_t)slice * cols + c0 + threadIdx.x, s, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -930,7 +933,7 @@ int launch_amax(const void* x, int64_t numel, int in_type, int fmt, void* ring, 
   return check_launch("amax_kernel");
 }
 
-// Row slices per 64-column strip: enough blocks to cover the CUs four times
+// Row slices per column strip: enough blocks to cover the CUs four times
 // over, each slice at least 32 rows.  A function of the shape only, so the
 // summation order (and the result) is fixed for a shape.
 int bias_grad_slices(int64_t rows, int64_t cols) {
@@ -942,7 +945,7 @@ int bias_grad_slices(int64_t rows, int64_t cols) {
   return (int)(s < 1 ? 1 : s);
 }
 
-// Workspace: one ticket per 64-column strip, then the slices' partial sums.
+// Workspace: one ticket per column strip, then the slices' partial sums.
 size_t bias_grad_tickets_bytes(int64_t cols) {
   const int64_t strips = (cols + kGradCols - 1) / kGradCols;
   return ((size_t)strips * 4 + 255) & ~(size_t)255;
