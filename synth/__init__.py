@@ -2,7 +2,7 @@
 
 This module holds random-number recipes only: no quantization, scaling or GEMM
 arithmetic.  Both the HIP path and the oracle receive the same host arrays
-made here.
+made here (or, for bf16_normal_device, the same device tensor's bits).
 
 Recipe (the pages train on their own models and data, which are not
 available, so every tensor is synthetic with the shapes of the pages'
@@ -34,6 +34,20 @@ def bf16_normal(shape, seed, sigma=1.0, outliers=False):
         mask = torch.rand(tuple(shape), generator=g) < 0.01
         x = torch.where(mask, x * 50.0, x)
     return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_normal_device(shape, seed, sigma=1.0, outliers=False, device="cuda"):
+    """The bf16_normal recipe drawn on the GPU from a device generator seeded
+    with `seed` (a different stream of numbers than bf16_normal's), as a bf16
+    device tensor: for workloads too large to draw on the host at every step.
+    Whoever checks a result against the oracle hands it this tensor's bits,
+    copied to the host."""
+    g = torch.Generator(device).manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32) * float(sigma)
+    if outliers:
+        mask = torch.rand(tuple(shape), generator=g, device=device) < 0.01
+        x = torch.where(mask, x * 50.0, x)
+    return x.to(torch.bfloat16)
 
 
 def bf16_normal_sequence(shapes, seed, sigma=1.0):

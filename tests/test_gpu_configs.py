@@ -26,8 +26,15 @@ class Side:
 
     def quantize(self, x_bits, check_codes=True):
         """Quantize on the GPU and in the oracle; returns (device codes,
-        oracle codes or None); the ring states are compared bit for bit."""
-        q = self.ds.fp8_quantize(to_dev_bf16(x_bits), self.fmt, self.ring)
+        oracle codes or None); the ring states are compared bit for bit.
+        x_bits: host bf16 bit patterns, or a bf16 device tensor whose bits
+        the oracle then receives copied to the host."""
+        if isinstance(x_bits, torch.Tensor):
+            x_dev = x_bits
+            x_bits = x_dev.view(torch.int16).cpu().numpy().view(np.uint16)
+        else:
+            x_dev = to_dev_bf16(x_bits)
+        q = self.ds.fp8_quantize(x_dev, self.fmt, self.ring)
         if check_codes:
             codes, self.ref = oracle.quantize_step(self.ref, x_bits)
         else:
