@@ -288,6 +288,13 @@ __device__ __forceinline__ bool fold_amax(RingHeader* ring, uint32_t amag_f32, u
                                           uint32_t* a) {
   const uint32_t bmax = block_max(amag_f32, red);
   if (threadIdx.x >= 64) return false;
+  if (G == 1) {
+    // The only block: its max is the launch's, and the tree's words are
+    // never touched (they stay zero), which saves three dependent round
+    // trips to the device-scope atomics on small tensors.
+    *a = __builtin_amdgcn_readfirstlane(bmax);
+    return true;
+  }
   uint32_t last = 0u, v = 0u;
   if (threadIdx.x == 0 && climb_tree(ring, bmax, G, b)) {
     v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
