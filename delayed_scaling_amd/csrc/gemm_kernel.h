@@ -1197,13 +1197,17 @@ GemmFn pick_large(int tile, int fa, int fb) {
   }
 }
 
+// The 256x128 / 128x256 tiles with both operands crosswise (TN) run one
+// workgroup per CU: at two, the transposed fragment reads leave too few
+// registers and the compiler spills hundreds of them.
 template <bool AKC, bool BKC>
 GemmFn pick_small(int tile, int fa, int fb) {
+  constexpr int kOccRect = AKC || BKC ? 2 : 1;
   switch (tile) {
     case 1: return pick_fmt<128, 128, 2, 2, 4, 2, AKC, BKC>(fa, fb);
     case 2: return pick_fmt<64, 64, 2, 2, 4, 4, AKC, BKC>(fa, fb);
-    case 3: return pick_fmt<256, 128, 2, 2, 3, 2, AKC, BKC>(fa, fb);
-    default: return pick_fmt<128, 256, 2, 2, 3, 2, AKC, BKC>(fa, fb);
+    case 3: return pick_fmt<256, 128, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
+    default: return pick_fmt<128, 256, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
   }
 }
 
