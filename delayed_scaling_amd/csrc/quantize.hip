@@ -15,10 +15,10 @@
 //
 // Each quantize launch streams x once (16-byte loads), so the kernels are
 // bound by HBM.  Each block reduces max|x| over its elements and climbs a
-// two-level completion tree kept in the ring's scratch lines (per-group max +
-// ticket, then a top-level max + ticket); the block holding the last
-// top-level ticket finalizes the ring and every scratch word is back at zero
-// for the next call on the same stream.
+// completion tree kept in the ring's scratch lines (a per-group max + ticket,
+// then a top-level ticket; a one-block launch skips it); the block holding
+// the last top-level ticket finalizes the ring and every scratch word is back
+// at zero for the next call on the same stream.
 #include <atomic>
 
 #include "device_common.h"
@@ -236,26 +236,33 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* red) {
   return r;
 }
 
-// Two-level completion tree, called by thread 0 of every block with the
-// block's max |x| as float32 bits; G blocks take part, this one is number b.
-// Block b belongs to group b % kRingGroups; each group has its own cache line
-// holding a running max and a ticket.  All words are device-scope atomics,
-// performed where every XCD sees them.  A ticket is taken only after the max
-// it covers has been performed (its returned value is waited for), so the
-// block drawing a group's last ticket reads a max that covers the whole
-// group, and the block drawing the last top-level ticket reads the max of all
-// groups.  No release/acquire fence is needed: the only data handed between
-// blocks are the atomic words themselves.
-__device__ bool climb_tree(RingHeader* ring, uint32_t bmax, int G, int b) {
+// Completion tree, called by thread 0 of every block with the block's max
+// |x| as float32 bits; G blocks take part, this one is number b.  All words
+// are device-scope atomics, performed where every XCD sees them, and a ticket
+// is taken only after the max (or ticket) it covers has been performed (its
+// returned value is waited for).  No release/acquire fence is needed: the
+// only data handed between blocks are the atomic words themselves.
+//  * At most kFlatTree blocks: each block takes the top-level max, then the
+//    top-level ticket.  Returns kTopMax in the block drawing the last ticket:
+//    the top-level max then covers every block.
+//  * More: block b belongs to group b % kRingGroups, whose 64-byte line
+//    holds a running max and a ticket; each block takes its group's max, then
+//    the group's ticket, and the block drawing a group's last ticket takes a
+//    top-level ticket.  Returns kGroupMax in the block drawing the last
+//    top-level ticket: every group's max is then final (each of its members
+//    took it before its group ticket, and the group's last member took the
+//    top-level ticket after all of those), so the launch's max is the max of
+//    the group words.  Four dependent round trips on the last block's path.
+constexpr int kNotLast = 0, kTopMax = 1, kGroupMax = 2;
+__device__ int climb_tree(RingHeader* ring, uint32_t bmax, int G, int b) {
   if (G <= kFlatTree) {
-    // Few blocks: every block goes straight to the top-level words.
     const uint32_t prev = __hip_atomic_fetch_max(&ring->amax_bits, bmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_returned(prev);
     const uint32_t t = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_returned(t);
-    return t == (uint32_t)G - 1;
+    return t == (uint32_t)G - 1 ? kTopMax : kNotLast;
   }
-  const int ngroups = G < kRingGroups ? G : kRingGroups;
+  static_assert(kFlatTree >= kRingGroups, "a two-level launch fills every group");
   const int g = b % kRingGroups;
   const uint32_t members = (uint32_t)((G - g + kRingGroups - 1) / kRingGroups);
   RingGroup* grp = ring_groups(ring) + g;
@@ -263,20 +270,10 @@ __device__ bool climb_tree(RingHeader* ring, uint32_t bmax, int G, int b) {
   wait_returned(prev);
   const uint32_t t = __hip_atomic_fetch_add(&grp->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   wait_returned(t);
-  if (t != members - 1) return false;
-  // Every member has performed its max and taken its ticket, so this block
-  // alone touches the group line now: read it, then clear it.  (Plain atomic
-  // loads and stores: an exchange whose returned value shared a register with
-  // its data was measured returning the new value on this target.)
-  const uint32_t gmax = __hip_atomic_load(&grp->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_returned(gmax);
-  __hip_atomic_store(&grp->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(&grp->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t prev2 = __hip_atomic_fetch_max(&ring->amax_bits, gmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_returned(prev2);
+  if (t != members - 1) return kNotLast;
   const uint32_t t2 = __hip_atomic_fetch_add(&ring->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   wait_returned(t2);
-  return t2 == (uint32_t)ngroups - 1;
+  return t2 == (uint32_t)kRingGroups - 1 ? kGroupMax : kNotLast;
 }
 
 // Called by every thread at the end of a launch of G blocks (this one number
@@ -295,15 +292,33 @@ __device__ __forceinline__ bool fold_amax(RingHeader* ring, uint32_t amag_f32, u
     *a = __builtin_amdgcn_readfirstlane(bmax);
     return true;
   }
-  uint32_t last = 0u, v = 0u;
-  if (threadIdx.x == 0 && climb_tree(ring, bmax, G, b)) {
-    v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_returned(v);
-    last = 1u;
+  int kind = kNotLast;
+  if (threadIdx.x == 0) kind = climb_tree(ring, bmax, G, b);
+  kind = __builtin_amdgcn_readfirstlane(kind);
+  if (kind == kNotLast) return false;
+  uint32_t v = 0u;
+  if (kind == kTopMax) {
+    if (threadIdx.x == 0) {
+      v = __hip_atomic_load(&ring->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_returned(v);
+    }
+    v = __builtin_amdgcn_readfirstlane(v);
+  } else {
+    // Lane g reads group g's max, then clears the group's line: no other
+    // block touches it again in this launch.  (Plain atomic loads and
+    // stores: an exchange whose returned value shared a register with its
+    // data was measured returning the new value on this target.)
+    RingGroup* grp = ring_groups(ring) + threadIdx.x;
+    if (threadIdx.x < kRingGroups) {
+      v = __hip_atomic_load(&grp->amax_bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_returned(v);
+      __hip_atomic_store(&grp->amax_bits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&grp->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    v = __builtin_amdgcn_readfirstlane(wave_max(v));
   }
-  last = __builtin_amdgcn_readfirstlane(last);
-  *a = __builtin_amdgcn_readfirstlane(v);
-  return last != 0u;
+  *a = v;
+  return true;
 }
 
 __device__ __forceinline__ void clear_top(RingHeader* ring) {
