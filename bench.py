@@ -558,6 +558,38 @@ def main():
     g_avg = sum(g_ms) / len(g_ms)
     flops = 2.0 * n * n * n
     q_bytes = 6.0 * n * n       # two n x n bf16 tensors read, their codes written
+
+    def quantize_after(pred, reps=30):
+        """Median duration (us) of the step's quantize launch issued right
+        after pred(r) on the same stream (None: after the device went idle);
+        events bracket the quantize alone."""
+        evs = []
+        for i in range(reps):
+            r = i % rot
+            if pred is None:
+                torch.cuda.synchronize()
+            else:
+                pred(r)
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
+            ds.fp8_quantize_batch([A[r], B[r]], ds.E4M3, [ring_a, ring_b], outs=[A8[r], B8[r]])
+            e[1].record(stream)
+            evs.append(e)
+        torch.cuda.synchronize()
+        return spread([a.elapsed_time(b) for a, b in evs])["p50"]
+
+    q_after = {
+        "gemm": quantize_after(lambda r: ds.fp8_mm(A8[r], B8[r], ds.E4M3, ds.E4M3, ds.NT, n, n, n, ring_a, ring_b,
+                                                   out=C[r])),
+        "copy_256MiB": quantize_after(lambda r: cal_dst.copy_(cal_src)),
+        "quantize": quantize_after(lambda r: ds.fp8_quantize_batch([A[r], B[r]], ds.E4M3, [ring_a, ring_b],
+                                                                   outs=[A8[r], B8[r]])),
+        "idle": quantize_after(None),
+    }
+    q_after = {k: {"p50_us": v, "frac": round(q_bytes / (v * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+               for k, v in q_after.items()}
+    q_after["note"] = ("the same quantize launch after different predecessors: the step's GEMM, a streaming "
+                       "device copy, itself, or an idle device")
     gemm_tflops = flops / (g_avg * 1e-3) / 1e12
     q_gbps = q_bytes / (q_avg * 1e-3) / 1e9
     traffic = traffic_from_profile(GEMM_SOURCES, "kernel_source_sha256", "hbm_bytes_per_launch")
@@ -591,7 +623,8 @@ def main():
                               "traffic": q_traffic,
                               "kernel": "quantize_batch_kernel<E4M3>: A and B, each with its ring, one launch",
                               "bytes_per_launch": q_bytes,
-                              "avg_launch_us": round(q_avg * 1e3, 2), "launch_us": spread(q_ms)},
+                              "avg_launch_us": round(q_avg * 1e3, 2), "launch_us": spread(q_ms),
+                              "after_predecessor": q_after},
     }
     if not args.no_widened:
         del A, B, A8, B8, C, cal_src, cal_dst

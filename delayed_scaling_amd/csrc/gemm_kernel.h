@@ -456,7 +456,7 @@ __device__ __forceinline__ bool store_c_tile(const GemmKArgs& p, const v16f (&ac
             if (n + e < p.n) bias4[e] = bp[e];
         }
       } else if (p.bias_kind >= 3) {
-        // 8-bit bias: fl32(dec(code) * bias_scale_inv), after the operand scaling.
+        // 8-bit bias: fl32(dec(code) * bias_scale_inv), added to acc * alpha.
         const uint8_t* bp = static_cast<const uint8_t*>(p.bias) + n;
         const float bsi = p.bias_scale_inv[0];
         uint32_t w = 0;

@@ -3,9 +3,9 @@
 // bias-gradient column sum.
 //
 // Pages (AstrAI commit histories):
-//  * astrai/extension/fp8.py @4dc5e923, ring-finalize entry: the last block
-//    to finish folds the amax into the history, reduces the window and
-//    publishes the next scale, so the update costs no extra launch;
+//  * astrai/extension/fp8.py @4dc5e923, ring-finalize entry: the history
+//    update and the next scale are computed inside the quantize launch, by
+//    whichever block completes last, rather than by a launch of their own;
 //  * fp8.py @f4c44ebf: the quantize is templated on its input type (bf16,
 //    fp16, fp32); the bias gradient is a column sum taken only when needed,
 //    over a dequantized gradient when the gradient is pre-quantized;

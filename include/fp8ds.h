@@ -37,8 +37,8 @@ typedef enum { FP8DS_NT = 0, FP8DS_NN = 1, FP8DS_TN = 2 } fp8ds_layout;
 
 /* Bias storage (bias-fusion entry, fp8.py history @f4c44ebf): none, bf16[N]
  * or fp32[N], or 8-bit codes[N] dequantized as dec(code) * bias_scale_inv
- * (history of test_fp8_mma.py, bias_scale entry); added in fp32 before the
- * single bf16 rounding. */
+ * (history of test_fp8_mma.py, bias_scale entry); the sum acc * alpha + bias
+ * is formed in fp32 and rounded to bf16 once. */
 typedef enum {
   FP8DS_BIAS_NONE = 0,
   FP8DS_BIAS_BF16 = 1,

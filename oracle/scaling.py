@@ -101,8 +101,9 @@ def next_scale(hist, fmt, old_scale):
 
 def advance_ring(ring, a):
     """The ring update of one quantize call whose tensor had amax `a`:
-    fold a into hist[idx] and advance idx; publish the next scale from the
-    window; record 1/scale_used and the amax.  Returns the new ring."""
+    store a in hist[idx] and step idx; derive the next scale from the
+    window's maximum; record 1/scale_used and the amax.  Returns the new
+    ring."""
     r = ring.copy()
     s_used = np.float32(r.scale)
     r.hist[r.idx] = np.float32(a)

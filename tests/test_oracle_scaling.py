@@ -103,7 +103,7 @@ def test_window_wraps_and_keeps_last_hist_len_values():
 
 
 def test_scale_snapshot_does_not_leak_ratio():
-    """Two delayed steps with a changing amax: the reciprocal recorded by a
+    """Two steps of the delayed recipe whose amax differs: the reciprocal recorded by a
     step is that of the scale the step applied, so dequantizing with it gives
     back the inputs to within the format's half-ulp, while the published
     (next) scale differs by the amax ratio."""
