@@ -369,8 +369,10 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
 // columns per 8-column group of each 32 x 32 MFMA tile.
 //
 // A block inside C stores through LDS (store_c_staged) when the caller hands
-// over a free stage buffer (with a bias, only blocks of at most 8 MFMA tiles);
-// without one (a launch with K = 0) a block inside
+// over a free stage buffer (staged = true; with a bias, only blocks of at most
+// 8 MFMA tiles).  The flag is separate from the pointer because the buffer at
+// LDS offset 0 is a valid one, and a null test of an LDS pointer compares it
+// with 0.  Without a buffer (a launch with K = 0) a block inside
 // C with no bias takes the register path: two column groups are combined by
 // swapping half of them between the lane halves, so every lane stores 8
 // consecutive columns (16 bytes) and each store instruction writes 32 rows x
@@ -384,14 +386,15 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
 // for every load in flight, at the loop's next register reuse).
 template <int BM, int BN, int TM, int TN, int NW, int LPS, bool DRAIN = false>
 __device__ __forceinline__ bool store_c_tile(const GemmKArgs& p, const v16f (&acc)[TN][TM], int v, int r0, int c0,
-                                             int lane, int wave, float alpha, lds_char_t* stage_buf) {
+                                             int lane, int wave, float alpha, bool staged,
+                                             lds_char_t* stage_buf) {
   int bt, tmi, tni;
   map_tile(p, v, bt, tmi, tni);
   const int m0 = tmi * BM + r0, n0 = tni * BN + c0;
   uint16_t* cb = p.c + bt * p.stride_c;
   // (Blocks of 16 MFMA tiles, one wave per SIMD, stage no bias: its registers
   // make the compiler spill in the K loop.)
-  if (stage_buf && (TM * TN <= 8 || p.bias_kind == 0) && p.ldc_small && m0 + TM * 32 <= p.m &&
+  if (staged && (TM * TN <= 8 || p.bias_kind == 0) && p.ldc_small && m0 + TM * 32 <= p.m &&
       n0 + TN * 32 <= p.n) {
     store_c_staged<BM, BN, TM, TN, NW, LPS>(p, acc, m0, n0, cb, lane, wave, alpha, stage_buf);
     return true;
@@ -704,7 +707,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
   if (kt_total == 0) {          // K = 0: every output is bf16(bias) or zero
     const float alpha = make_alpha();
     for (int it = 0; it < my_tiles; ++it)
-      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, nullptr);
+      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, false, nullptr);
     return;
   }
 
@@ -810,7 +813,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
       stage(Read{}, s0 + kt + 1, kt + 2, fa1, fb1, fa0, fb0);
     }
     stage(NoRead{}, s0 + kt_total - 1, 0, fa0, fb0, fa1, fb1);
-    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha,
+    store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, true,
                                           buf(s0 + kt_total - 1 + D));
     // The staging reads have returned before the loads refill the area.  (The
     // loads after the last tile fetch nothing; skipping them with an early
@@ -1023,7 +1026,7 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
   if (units == 0) {
     const float alpha = make_alpha();
     for (int it = 0; it < my_tiles; ++it)
-      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, nullptr);
+      store_c_tile<BM, BN, TM, TN, NW, LPS>(p, acc, wg + it * G, r0, c0, lane, wave, alpha, false, nullptr);
     return;
   }
 
@@ -1129,7 +1132,7 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
     // trail the loads the next odd half-stage waits for, and its wait lets
     // them stay in flight.
     after_store = store_c_tile<BM, BN, TM, TN, NW, LPS, true>(p, acc, wg + it * G, r0, c0, lane, wave, alpha,
-                                                              slot(ld.lslot));
+                                                              true, slot(ld.lslot));
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
