@@ -293,7 +293,8 @@ int fp8_mm_with_grid(const fp8_mm_args* args, int tile, int max_workgroups, void
  * forward-carries-scale entry: the backward's two GEMMs).  When `first` is
  * NN and `second` is TN with the same fmt_a and fmt_b, both run in one launch
  * whose workgroups are split between them, so small GEMMs that each leave
- * most of the chip idle share it; any other pair runs as two launches in
+ * most of the chip idle share it, unless one of them is big enough for the
+ * four-wave 256x256 tile on its own; any other pair runs as two launches in
  * order.  Each argument set is validated as fp8_mm validates it, and neither
  * output may overlap the other problem's operands, bias or output
  * (FP8DS_EINVAL); nothing is launched on an error.  An empty problem (m or n
