@@ -168,9 +168,9 @@ int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t s
   const GemmProblem pp[2] = {p0, p1};
   const int t = choose_pair_tile(pp);
   // A problem that takes the four-wave 256x256 tile on its own runs faster
-  // there than in the pair kernel's eight-wave tile, by more than the second
-  // launch costs (dX 4096x4096x1024 + dW 1024x4096x4096: 41.3 us as two
-  // launches, 43.1 us as one; at 8192 tokens 87.3 against 97.2 us).  Every
+  // there than in the pair kernel's eight-wave tile, by at least what the
+  // second launch costs (dX 8192x4096x1024 + dW 1024x4096x8192: 88.7 us as
+  // two launches, 97.2 us as one; at 4096 tokens the two are level).  Every
   // tile gives the same bits, so the outputs do not depend on the choice.
   if (t == 6 && (choose_tile(p0) == 0 || choose_tile(p1) == 0)) {
     const int st = launch_gemm(p0, -1, 0, stream);
