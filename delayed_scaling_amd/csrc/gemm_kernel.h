@@ -345,9 +345,16 @@ __device__ __forceinline__ void store_c_staged(const GemmKArgs& p, const v16f (&
           val[q] = *(const lds_v4i_t*)((lds_char_t*)(uintptr_t)(row_at(r) + ((rc ^ (r % CH)) << 4)));
         }
         uint8_t* band = base + (uint32_t)j * 32u * ldc2 + cc * SC * 2u;
+        // Streaming stores: written normally, C's lines stay dirty in the
+        // Infinity Cache and the next kernel pays for their write-back (the
+        // 8192^2 quantize after an 8192^3 GEMM took 73.4 us after plain
+        // stores, 68.9 us after streaming ones, 64.7 us after another
+        // quantize; the GEMM itself ran 1.3 us faster).  A choice between
+        // the two at run time doubles this code and makes the 256x256
+        // four-wave kernel spill.
 #pragma unroll
         for (uint32_t q = 0; q < NR; ++q)
-          *reinterpret_cast<v4i*>(band + goff + q * RPI * ldc2) = val[q];
+          __builtin_nontemporal_store(val[q], reinterpret_cast<v4i*>(band + goff + q * RPI * ldc2));
         // One row band at a time: interleaving the bands holds more registers
         // than the K loop leaves free.
         __builtin_amdgcn_sched_barrier(0);

@@ -11,7 +11,7 @@ The forward's dequantization scales are kept aside when the forward runs
 (fp8.py @f4c44ebf, forward-carries-scale entry), so a later forward on the
 same rings cannot change what the backward dequantizes with: X and W are
 quantized in one batched launch that also writes both applied 1/scale values
-into a small tensor the backward keeps.  Every arithmetic step runs in the
+next to the codes, in the one buffer the backward keeps.  Every arithmetic step runs in the
 library's kernels; this module only allocates outputs and orders the calls
 on the current stream.
 
@@ -57,14 +57,24 @@ def _input(t, name, dev):
 
 def _mm(a, b, c, fmt_a, layout, m, n, k, sa, sb, bias=None, bias_kind=BIAS_NONE):
     """The argument struct of one dense GEMM (formats fmt_a x E4M3) over
-    contiguous operands the layer allocated."""
+    contiguous operands the layer allocated (a, b, c: device addresses)."""
     a_cols = m if layout == TN else k
     b_cols = k if layout == NT else n
     a_rows = k if layout == TN else m
     b_rows = n if layout == NT else k
-    return _MMARGS.pack(a.data_ptr(), b.data_ptr(), c.data_ptr(), fmt_a, E4M3, layout, bias_kind, m, n, k, 1,
+    return _MMARGS.pack(a, b, c, fmt_a, E4M3, layout, bias_kind, m, n, k, 1,
                         a_cols, b_cols, n, a_rows * a_cols, b_rows * b_cols, m * n, sa, sb,
                         0 if bias is None else bias.data_ptr(), 0)
+
+
+def _codes_layout(t, n_in, n_out):
+    """Byte offsets of the forward's saved buffer: X's codes [t, n_in], W's
+    codes [n_out, n_in], then the two applied 1/scale values (each piece
+    256-byte aligned).  One allocation instead of three: the layer's host
+    time per call is mostly fixed costs like these."""
+    wo = (t * n_in + 255) & ~255
+    so = wo + ((n_out * n_in + 255) & ~255)
+    return wo, so, so + 8
 
 
 class _Fp8LinearFn(torch.autograd.Function):
@@ -79,12 +89,12 @@ class _Fp8LinearFn(torch.autograd.Function):
         w2 = _input(w, "weight", dev)
         t = x2.shape[0]
         L, st = lib(), _stream(None)
-        s = torch.empty(2, dtype=torch.float32, device=dev)   # applied 1/scale of X and W
-        sp = s.data_ptr()
-        x8 = torch.empty((t, n_in), dtype=torch.uint8, device=dev)
-        w8 = torch.empty((n_out, n_in), dtype=torch.uint8, device=dev)
-        jx = _QJOB.pack(x2.data_ptr(), x2.numel(), state.ring_x._bufp, x8.data_ptr(), sp)
-        jw = _QJOB.pack(w2.data_ptr(), w2.numel(), state.ring_w._bufp, w8.data_ptr(), sp + 4)
+        wo, so, nbytes = _codes_layout(t, n_in, n_out)
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)   # X codes | W codes | 1/scale of X, W
+        x8 = saved.data_ptr()
+        w8, sp = x8 + wo, x8 + so
+        jx = _QJOB.pack(x2.data_ptr(), x2.numel(), state.ring_x._bufp, x8, sp)
+        jw = _QJOB.pack(w2.data_ptr(), w2.numel(), state.ring_w._bufp, w8, sp + 4)
         if x2.dtype == w2.dtype:
             _check(L.fp8_quantize_batch(jx + jw, 2, _IN_TYPE[x2.dtype], E4M3, st))
         else:
@@ -97,8 +107,8 @@ class _Fp8LinearFn(torch.autograd.Function):
                 raise Fp8dsError("bias must be a bf16 or fp32 tensor of out_features elements on the layer's GPU")
             b = b if b.is_contiguous() else b.contiguous()
         y = torch.empty((t, n_out), dtype=torch.bfloat16, device=dev)
-        _check(L.fp8_mm(_mm(x8, w8, y, E4M3, NT, t, n_out, n_in, sp, sp + 4, b, bias_kind), st))
-        ctx.save_for_backward(x8, w8, s)
+        _check(L.fp8_mm(_mm(x8, w8, y.data_ptr(), E4M3, NT, t, n_out, n_in, sp, sp + 4, b, bias_kind), st))
+        ctx.save_for_backward(saved)
         ctx.state = state
         ctx.dims = (t, n_in, n_out)
         ctx.x_shape = x.shape
@@ -107,26 +117,29 @@ class _Fp8LinearFn(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, gy):
-        x8, w8, s = ctx.saved_tensors
+        saved, = ctx.saved_tensors
         t, n_in, n_out = ctx.dims
         state = ctx.state
-        dev = x8.device
+        dev = saved.device
+        wo, so, _ = _codes_layout(t, n_in, n_out)
+        x8 = saved.data_ptr()
+        w8, sp = x8 + wo, x8 + so
         g2 = gy.reshape(-1, n_out)
         if g2.dtype != torch.bfloat16 or not g2.is_contiguous():
             g2 = g2.to(torch.bfloat16).contiguous()
         L, st = lib(), _stream(None)
-        sp = s.data_ptr()
-        g8 = torch.empty((t, n_out), dtype=torch.uint8, device=dev)
-        _check(L.fp8_quantize(g2.data_ptr(), g2.numel(), E5M2, state.ring_g._bufp, g8.data_ptr(), st))
+        g8t = torch.empty((t, n_out), dtype=torch.uint8, device=dev)
+        g8 = g8t.data_ptr()
+        _check(L.fp8_quantize(g2.data_ptr(), g2.numel(), E5M2, state.ring_g._bufp, g8, st))
         sg = state.ring_g._sinv
         dx = dw = db = None
         need_x, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
         if need_x:
             dx = torch.empty((t, n_in), dtype=torch.bfloat16, device=dev)
-            ax = _mm(g8, w8, dx, E5M2, NN, t, n_in, n_out, sg, sp + 4)
+            ax = _mm(g8, w8, dx.data_ptr(), E5M2, NN, t, n_in, n_out, sg, sp + 4)
         if need_w:
             dw = torch.empty((n_out, n_in), dtype=torch.bfloat16, device=dev)
-            aw = _mm(g8, x8, dw, E5M2, TN, n_out, n_in, t, sg, sp)
+            aw = _mm(g8, x8, dw.data_ptr(), E5M2, TN, n_out, n_in, t, sg, sp)
         if need_x and need_w:
             _check(L.fp8_mm_pair(ax, aw, st))                   # one launch for both
         elif need_x:
