@@ -261,10 +261,19 @@ def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
         return e0.elapsed_time(e1) / steps
 
     res = {}
+    # Eager steps are bound by host time, which drifts while the process
+    # runs: the two paths alternate over three rounds, and each reports the
+    # mean of its rounds.
     for name, mods in (("fp8", fp8), ("bf16", bf16)):
-        for _ in range(2):
+        for _ in range(3):
             run(mods)
-        res[name + "_eager"] = timed(lambda: run(mods))
+    eager = {"fp8": [], "bf16": []}
+    for _ in range(3):
+        for name, mods in (("fp8", fp8), ("bf16", bf16)):
+            eager[name].append(timed(lambda: run(mods)))
+    for name in eager:
+        res[name + "_eager"] = sum(eager[name]) / len(eager[name])
+    for name, mods in (("fp8", fp8), ("bf16", bf16)):
         # The same step captured once in a HIP graph and replayed: no host work per call.
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -284,6 +293,7 @@ def measure_linear_step(stream, tokens=2048, dim=1024, layers=12, steps=5):
             "fp8_tflops": round(flops / (res["fp8"] * 1e-3) / 1e12, 1),
             "bf16_tflops": round(flops / (res["bf16"] * 1e-3) / 1e12, 1),
             "eager_fp8_ms_per_step": round(res["fp8_eager"], 3), "eager_bf16_ms_per_step": round(res["bf16_eager"], 3),
+            "eager_rounds_ms": {k: [round(v, 3) for v in eager[k]] for k in eager},
             "gemm_flops": flops}
 
 
