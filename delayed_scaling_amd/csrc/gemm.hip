@@ -26,9 +26,11 @@ struct TileCfg {
 // MFMA; the eight-wave 256x256 tiles give every SIMD two waves of a 128x64 /
 // 64x128 block (the pair kernel's large tile); 256x128 / 128x256 run two
 // workgroups per CU (3 stages, 72 KiB each);
-// 128x128 and 64x64 serve problems too small to fill the chip.
+// 128x128 and 64x64 serve problems too small to fill the chip; the 128x128
+// tile on 128-byte K units (five 16 KiB slots, two workgroups per CU) is the
+// one the automatic choice takes, the general kernel's stays for tests.
 constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
-                              {128, 256, 4}, {256, 256, 8}, {256, 256, 8}};
+                              {128, 256, 4}, {256, 256, 8}, {256, 256, 8}, {128, 128, 4}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // The kernel of one tile, layout and format pair, from its picker file.
@@ -42,36 +44,49 @@ GemmFn kernel_for(int tile, int layout, int fa, int fb) {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile choice by grid size, from per-shape timings on 256 CUs:
-//  * a 256x256 tile when its grid fills at least three quarters of the CUs
-//    (4096x3072x1024: 18.6 us against 21.0 us in 128x128 tiles);
-//  * else 128x128 when its grid fills them, or half-fills them with K >= 2048
-//    (a half-empty chip of 128x128 tiles beats a full one of 64x64 tiles once
-//    the K loop is long enough to amortize their higher per-tile rate);
+//  * a 256x256 tile when its grid fills at least three quarters of the CUs,
+//    except (single GEMMs) when K <= 1024 and its last round of tiles is
+//    partial: there the 128x128 tile on 128-byte K units, two workgroups per
+//    CU, ends sooner (4096x3072x1024, 192 tiles: 15.2 against 17.8 us;
+//    8192x3072x1024, 384 tiles: 25.5 against 30.9 us; with a bias 16.7 and
+//    28.9 against 20.6 and 34.9 us), while on whole rounds the two are level
+//    and with K = 4096 the 256x256 tile is clearly faster (4096^3: 50 against
+//    62 us);
+//  * else the 128x128 tile on 128-byte units when its grid fills the CUs, or
+//    half-fills them with K >= 2048 (a half-empty chip of 128x128 tiles
+//    beats a full one of 64x64 tiles once the K loop is long enough to
+//    amortize their higher per-tile rate); the unit tile ran 0-25 % faster
+//    than the general kernel's 128x128 tile on every layer shape measured
+//    (8192x1024x4096 NT: 29.4 against 39.0 us), with the same bits;
 //  * else 64x64, the most tiles.
 int64_t tile_count(const GemmProblem& p, int t) {
   return cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch;
 }
 
 // The rule over a launch's total tile count and (shortest) K.
-int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k, int big) {
+int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k, int big,
+             bool partial_round_rule) {
   constexpr int64_t kCUs = 256;
-  if (4 * count(ps, big) >= 3 * kCUs) return big;
-  const int64_t t1 = count(ps, 1);
-  if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 1;
+  const int64_t tb = count(ps, big);
+  if (4 * tb >= 3 * kCUs && !(partial_round_rule && k <= 1024 && tb % kCUs != 0)) return big;
+  const int64_t t1 = count(ps, 7);
+  if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 7;
   return 2;
 }
 
 // Large launches take the four-wave 256x256 tile without a bias and the
 // eight-wave one, which stages its bias epilogue through LDS, with one.
 int choose_tile(const GemmProblem& p) {
-  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6);
+  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6,
+                  true);
 }
 
 // For a fused pair: the same rule over both problems' tiles and the shorter K
-// (the pair kernel has the eight-wave 256x256 tile).
+// (the pair kernel has the eight-wave 256x256 tile), without the
+// partial-round exception (not measured on pairs).
 int choose_pair_tile(const GemmProblem (&pp)[2]) {
   return tile_for([](const GemmProblem* q, int t) { return tile_count(q[0], t) + tile_count(q[1], t); }, pp,
-                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6);
+                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6, false);
 }
 
 // Workgroups of one kernel that fit on the device at once (CUs x occupancy),

@@ -67,16 +67,16 @@ typedef void (*GemmPairFn)(GemmKArgs, GemmKArgs, int);
 
 // Kernel pickers, one per translation unit.  tile indexes the family of
 // gemm.hip (0: 256x256 four waves, 1: 128x128, 2: 64x64, 3: 256x128,
-// 4: 128x256, 5 / 6: 256x256 eight waves as 2x4 / 4x2); fa / fb are the
-// operand formats (0 E4M3, 1 E5M2).  "large" covers tiles 0, 5 and 6,
-// "small" tiles 1 to 4.
+// 4: 128x256, 5 / 6: 256x256 eight waves as 2x4 / 4x2, 7: 128x128 on
+// 128-byte K units); fa / fb are the operand formats (0 E4M3, 1 E5M2).
+// "large" covers tiles 0, 5 and 6, "small" tiles 1 to 4 and 7.
 GemmFn gemm_fn_nt_large(int tile, int fa, int fb);
 GemmFn gemm_fn_nt_small(int tile, int fa, int fb);
 GemmFn gemm_fn_nn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_nn_small(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_small(int tile, int fa, int fb);
-// The fused NN + TN pair (a layer's dX and dW) for tiles 1, 2 and 6.
+// The fused NN + TN pair (a layer's dX and dW) for tiles 1, 2, 6 and 7.
 GemmPairFn gemm_pair_fn(int tile, int fa, int fb);
 
 namespace {
@@ -891,10 +891,10 @@ __device__ __forceinline__ v8i frag_k128(const lds_char_t* slot, int base, int l
 
 // The same fragment from a crosswise slot [128 k][256 B]: half h is k rows
 // 64 h .. 64 h + 63, read as in the general kernel.
-template <bool KC>
+template <bool KC, int R>
 __device__ __forceinline__ v8i frag_u128(const lds_char_t* slot, int base, int lane, int h) {
   if constexpr (KC) return frag_k128(slot, base, lane, h);
-  else return frag_mn<16>(slot + h * 64 * 256, base, lane);
+  else return frag_mn<R / 16>(slot + h * 64 * R, base, lane);
 }
 
 // Load l of a wave covers slots i = (l * NW + wave) * 64 + lane: for a
@@ -905,22 +905,25 @@ __device__ __forceinline__ v8i frag_u128(const lds_char_t* slot, int base, int l
 // Rows of a K-contiguous operand past M (N) start past the end of the
 // operand, where the buffer descriptor's range check returns zeros; columns
 // of a crosswise operand past N (M) are marked kOOB in the base.
-template <bool KC, int NW>
+template <bool KC, int NW, int R>
 __device__ __forceinline__ uint32_t u128_base(int wave, int lane, int mn0, int mn_lim, uint32_t ld) {
   if constexpr (KC) {
     const int row = 8 * wave + (lane >> 3), lch = (lane & 7) ^ swz_k128(row);
     return (uint32_t)row * ld + (uint32_t)(lch << 4);
   } else {
-    const int kr = 4 * wave + (lane >> 4), lch = (lane & 15) ^ swz_mn<16>(kr);
+    constexpr int CH = R / 16, KR = 64 / CH;   // chunks of a k row; k rows per wave and load
+    const int kr = KR * wave + lane / CH, lch = (lane % CH) ^ swz_mn<CH>(kr);
     return mn0 + (lch << 4) < mn_lim ? (uint32_t)kr * ld + (uint32_t)(lch << 4) : kOOB;
   }
 }
-template <bool KC>
-__device__ __forceinline__ uint32_t u128_step(uint32_t ld) { return KC ? 32u * ld : 16u * ld; }
+template <bool KC, int NW, int R>
+__device__ __forceinline__ uint32_t u128_step(uint32_t ld) {
+  return KC ? (uint32_t)(8 * NW) * ld : (uint32_t)(NW * 64 / (R / 16)) * ld;
+}
 
-template <int NW, bool A_KC, bool B_KC>
+template <int NW, bool A_KC, bool B_KC, int R>
 struct UnitLoader {
-  static constexpr int SLOT = 256 * kKU;              // bytes of one slot
+  static constexpr int SLOT = R * kKU;                // bytes of one slot
   static constexpr int LPS = SLOT / 1024 / NW;        // loads per wave and load stage
   static_assert(NW == 4, "the slot mapping assumes four waves");
   int it = 0, j = 0, wg = 0, G = 1, units = 1;
@@ -931,13 +934,13 @@ struct UnitLoader {
   __device__ __forceinline__ void set_tile(const GemmKArgs& p, int v, int wave, int lane) {
     int bt, tmi, tni;
     map_tile(p, v, bt, tmi, tni);
-    const int m0 = tmi * 256, n0 = tni * 256;
+    const int m0 = tmi * R, n0 = tni * R;
     const uint32_t a_tile_off = A_KC ? (uint32_t)m0 * p.lda : (uint32_t)m0;
     const uint32_t b_tile_off = B_KC ? (uint32_t)n0 * p.ldb : (uint32_t)n0;
     ra = rsrc_words(p.a + bt * p.stride_a + a_tile_off, p.extent_a - a_tile_off);
     rb = rsrc_words(p.b + bt * p.stride_b + b_tile_off, p.extent_b - b_tile_off);
-    a_base = u128_base<A_KC, NW>(wave, lane, m0, p.m, p.lda);
-    b_base = u128_base<B_KC, NW>(wave, lane, n0, p.n, p.ldb);
+    a_base = u128_base<A_KC, NW, R>(wave, lane, m0, p.m, p.lda);
+    b_base = u128_base<B_KC, NW, R>(wave, lane, n0, p.n, p.ldb);
   }
 
   __device__ __forceinline__ void init(const GemmKArgs& p, int wave, int lane, int wg_, int G_) {
@@ -955,7 +958,7 @@ struct UnitLoader {
     constexpr bool KC = OP == 0 ? A_KC : B_KC;
     const uint32_t ld = OP == 0 ? p.lda : p.ldb;
     const uint32_t soff = KC ? (uint32_t)(u * kKU) : (uint32_t)(u * kKU) * ld;
-    const uint32_t voff = (OP == 0 ? a_base : b_base) + (uint32_t)l * u128_step<KC>(ld);
+    const uint32_t voff = (OP == 0 ? a_base : b_base) + (uint32_t)l * u128_step<KC, NW, R>(ld);
     load_lds16(OP == 0 ? ra : rb, lds, voff, soff);
   }
 
@@ -986,11 +989,11 @@ struct UnitLoader {
 // (bytes of the operand past K, or zeros past its end): in a K-contiguous
 // slot bytes kin .. 127 of every row (chunk c of row r at c ^ swz_k128(r)),
 // in a crosswise slot the 256-byte k rows kin .. 127.
-template <bool KC, int kThreads>
+template <bool KC, int kThreads, int R>
 __device__ __forceinline__ void zero_k_tail_slot(lds_char_t* slot, int kin) {
   const v4i z = v4i{0, 0, 0, 0};
   if constexpr (KC) {
-    for (int r = threadIdx.x; r < 256; r += kThreads) {
+    for (int r = threadIdx.x; r < R; r += kThreads) {
       lds_char_t* rp = slot + r * kKU;
       const int sw = swz_k128(r);
 #pragma nounroll
@@ -1000,16 +1003,16 @@ __device__ __forceinline__ void zero_k_tail_slot(lds_char_t* slot, int kin) {
       for (int b = kin & 15; b != 0 && b < 16; ++b) cp[b] = 0;
     }
   } else {
-    for (int i = threadIdx.x; i < (kKU - kin) * 16; i += kThreads) *(lds_v4i_t*)(slot + kin * 256 + i * 16) = z;
+    for (int i = threadIdx.x; i < (kKU - kin) * (R / 16); i += kThreads) *(lds_v4i_t*)(slot + kin * R + i * 16) = z;
   }
 }
 
-template <bool A_KC, bool B_KC, int FA, int FB>
+template <bool A_KC, bool B_KC, int FA, int FB, int R>
 __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* smem, int wg, int G) {
-  constexpr int BM = 256, BN = 256, NW = 4, kThreads = 256;
-  constexpr int WM = 128, WN = 128, TM = 4, TN = 4, NM = TM * TN, NF = TM + TN;
+  constexpr int BM = R, BN = R, NW = 4, kThreads = 256;
+  constexpr int WM = R / 2, WN = R / 2, TM = WM / 32, TN = WN / 32, NM = TM * TN, NF = TM + TN;
   constexpr int kFragMfmas = 3 * NM / 4;
-  using Loader = UnitLoader<NW, A_KC, B_KC>;
+  using Loader = UnitLoader<NW, A_KC, B_KC, R>;
   constexpr int SLOT = Loader::SLOT, LPS = Loader::LPS;
 
   const int lane = threadIdx.x & 63;
@@ -1046,16 +1049,16 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
     const lds_char_t* sa = slot(rslot);
     const lds_char_t* sb = slot(next_slot(rslot));
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = frag_u128<A_KC>(sa, r0 + i * 32, lane, h);
+    for (int i = 0; i < TM; ++i) fa[i] = frag_u128<A_KC, R>(sa, r0 + i * 32, lane, h);
 #pragma unroll
-    for (int i = 0; i < TN; ++i) fb[i] = frag_u128<B_KC>(sb, c0 + i * 32, lane, h);
+    for (int i = 0; i < TN; ++i) fb[i] = frag_u128<B_KC, R>(sb, c0 + i * 32, lane, h);
   };
   // Zero the K padding of the unit about to be read when it is a partial
   // last unit of a tile (the slots are visible: its loads have landed).
   auto fix_tail_u = [&](bool last_unit) __attribute__((always_inline)) {
     if (kin != 0 && last_unit) {
-      zero_k_tail_slot<A_KC, kThreads>(slot(rslot), kin);
-      zero_k_tail_slot<B_KC, kThreads>(slot(next_slot(rslot)), kin);
+      zero_k_tail_slot<A_KC, kThreads, R>(slot(rslot), kin);
+      zero_k_tail_slot<B_KC, kThreads, R>(slot(next_slot(rslot)), kin);
       lds_barrier();
     }
   };
@@ -1098,8 +1101,8 @@ __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* s
       // they have landed when the next half-stage starts.
 #pragma unroll
       for (int f = slot_items(q, kFragMfmas, NF, 1); f < slot_items(q + 1, kFragMfmas, NF, 1); ++f) {
-        if (f < TM) na[f] = frag_u128<A_KC>(sa, r0 + f * 32, lane, H);
-        else nb[f - TM] = frag_u128<B_KC>(sb, c0 + (f - TM) * 32, lane, H);
+        if (f < TM) na[f] = frag_u128<A_KC, R>(sa, r0 + f * 32, lane, H);
+        else nb[f - TM] = frag_u128<B_KC, R>(sb, c0 + (f - TM) * 32, lane, H);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1156,7 +1159,27 @@ __global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_kernel(GemmKArgs p) 
 template <bool A_KC, bool B_KC, int FA, int FB>
 __global__ __launch_bounds__(256, 1) void gemm_u128_kernel(GemmKArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 256 * kKU];
-  gemm_body_u128<A_KC, B_KC, FA, FB>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
+  gemm_body_u128<A_KC, B_KC, FA, FB, 256>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// The same body on a 128x128 tile (each wave a 64x64 block; five 16 KiB
+// slots, two workgroups per CU).
+template <bool A_KC, bool B_KC, int FA, int FB>
+__global__ __launch_bounds__(256, 2) void gemm_u128s_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 128 * kKU];
+  gemm_body_u128<A_KC, B_KC, FA, FB, 128>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// A layer's dX and dW in one launch on that tile (workgroups [0, g0) the
+// first problem, the rest the second, as in gemm_pair_kernel below).
+template <bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1, int FA, int FB>
+__global__ __launch_bounds__(256, 2) void gemm_pair_u128s_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 128 * kKU];
+  const int wg = (int)blockIdx.x;
+  if (wg < g0)
+    gemm_body_u128<A_KC0, B_KC0, FA, FB, 128>(p0, (lds_char_t*)smem_raw, wg, g0);
+  else
+    gemm_body_u128<A_KC1, B_KC1, FA, FB, 128>(p1, (lds_char_t*)smem_raw, wg - g0, (int)gridDim.x - g0);
 }
 
 // Two independent problems in one launch (a layer's dX and dW): workgroups
@@ -1199,6 +1222,14 @@ GemmFn pick_u128(int fa, int fb) {
 }
 
 template <bool AKC, bool BKC>
+GemmFn pick_u128s(int fa, int fb) {
+  if (fa == 0 && fb == 0) return gemm_u128s_kernel<AKC, BKC, 0, 0>;
+  if (fa == 1 && fb == 0) return gemm_u128s_kernel<AKC, BKC, 1, 0>;
+  if (fa == 0 && fb == 1) return gemm_u128s_kernel<AKC, BKC, 0, 1>;
+  return gemm_u128s_kernel<AKC, BKC, 1, 1>;
+}
+
+template <bool AKC, bool BKC>
 GemmFn pick_large(int tile, int fa, int fb) {
   switch (tile) {
     case 5: return pick_fmt<256, 256, 2, 4, 4, 1, AKC, BKC>(fa, fb);
@@ -1217,6 +1248,7 @@ GemmFn pick_small(int tile, int fa, int fb) {
     case 1: return pick_fmt<128, 128, 2, 2, 4, 2, AKC, BKC>(fa, fb);
     case 2: return pick_fmt<64, 64, 2, 2, 4, 4, AKC, BKC>(fa, fb);
     case 3: return pick_fmt<256, 128, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
+    case 7: return pick_u128s<AKC, BKC>(fa, fb);
     default: return pick_fmt<128, 256, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
   }
 }
