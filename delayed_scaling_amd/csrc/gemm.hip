@@ -45,8 +45,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile choice by grid size, from per-shape timings on 256 CUs:
 //  * a 256x256 tile when its grid fills at least three quarters of the CUs,
-//    except (single GEMMs) when K <= 1024 and its last round of tiles is
-//    partial: there the 128x128 tile on 128-byte K units, two workgroups per
+//    except when K <= 1024 and its last round of tiles is partial: there the 128x128 tile on 128-byte K units, two workgroups per
 //    CU, ends sooner (4096x3072x1024, 192 tiles: 15.2 against 17.8 us;
 //    8192x3072x1024, 384 tiles: 25.5 against 30.9 us; with a bias 16.7 and
 //    28.9 against 20.6 and 34.9 us), while on whole rounds the two are level
@@ -82,11 +81,14 @@ int choose_tile(const GemmProblem& p) {
 }
 
 // For a fused pair: the same rule over both problems' tiles and the shorter K
-// (the pair kernel has the eight-wave 256x256 tile), without the
-// partial-round exception (not measured on pairs).
+// (the pair kernel has the eight-wave 256x256 tile).  The partial-round
+// exception holds for pairs too: the 12-layer step at 2048 tokens (whose MLP
+// down-projection pair has 192 tiles of 256x256 and K = 1024) went from
+// 2.58-2.59 to 2.50-2.52 ms, at 4096 tokens (that pair, 320 tiles, then runs
+// as one launch instead of two) from 3.53-3.59 to 3.50-3.52 ms.
 int choose_pair_tile(const GemmProblem (&pp)[2]) {
   return tile_for([](const GemmProblem* q, int t) { return tile_count(q[0], t) + tile_count(q[1], t); }, pp,
-                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6, false);
+                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6, true);
 }
 
 // Workgroups of one kernel that fit on the device at once (CUs x occupancy),
