@@ -35,7 +35,7 @@ ROWWISE, TRANSPOSED, DUAL = 0, 1, 2
 G_BF16, G_F16, G_F32, G_E4M3, G_E5M2 = 0, 1, 2, 3, 4
 _IN_TYPE = {torch.bfloat16: IN_BF16, torch.float16: IN_F16, torch.float32: IN_F32}
 TILES = {"256x256": 0, "128x128": 1, "64x64": 2, "256x128": 3, "128x256": 4, "256x256w8n": 5, "256x256w8": 6,
-         "128x128u": 7}
+         "128x128u": 7, "64x64u": 8}
 RING_HIST_OFFSET = 2112   # byte offset of hist[] in a ring (include/fp8ds.h)
 RING_GROUPS = 32          # completion-tree scratch lines after the 64-byte header
 

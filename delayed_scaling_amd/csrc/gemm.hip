@@ -27,10 +27,11 @@ struct TileCfg {
 // 64x128 block (the pair kernel's large tile); 256x128 / 128x256 run two
 // workgroups per CU (3 stages, 72 KiB each);
 // 128x128 and 64x64 serve problems too small to fill the chip; the 128x128
-// tile on 128-byte K units (five 16 KiB slots, two workgroups per CU) is the
-// one the automatic choice takes, the general kernel's stays for tests.
+// and 64x64 tiles on 128-byte K units (five 16 / 8 KiB slots, two / four
+// workgroups per CU) are the ones the automatic choice takes, the general
+// kernel's stay for tests.
 constexpr TileCfg kTiles[] = {{256, 256, 4}, {128, 128, 4}, {64, 64, 4}, {256, 128, 4},
-                              {128, 256, 4}, {256, 256, 8}, {256, 256, 8}, {128, 128, 4}};
+                              {128, 256, 4}, {256, 256, 8}, {256, 256, 8}, {128, 128, 4}, {64, 64, 4}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
 // The kernel of one tile, layout and format pair, from its picker file.
@@ -50,14 +51,17 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //    8192x3072x1024, 384 tiles: 25.5 against 30.9 us; with a bias 16.7 and
 //    28.9 against 20.6 and 34.9 us), while on whole rounds the two are level
 //    and with K = 4096 the 256x256 tile is clearly faster (4096^3: 50 against
-//    62 us);
+//    62 us); with K <= 512 the 128x128 unit tile wins on whole rounds too
+//    (64 x 512^3 batched: 12.6 against 14.3 us);
 //  * else the 128x128 tile on 128-byte units when its grid fills the CUs, or
 //    half-fills them with K >= 2048 (a half-empty chip of 128x128 tiles
 //    beats a full one of 64x64 tiles once the K loop is long enough to
 //    amortize their higher per-tile rate); the unit tile ran 0-25 % faster
 //    than the general kernel's 128x128 tile on every layer shape measured
 //    (8192x1024x4096 NT: 29.4 against 39.0 us), with the same bits;
-//  * else 64x64, the most tiles.
+//  * else 64x64 on 128-byte units, the most tiles (against the general
+//    kernel's 64x64 tile, same bits: 1024x1024x4096 NT 12.9 -> 10.8 us,
+//    1024x1536x2048 NN 10.3 -> 9.0 us, TN level).
 int64_t tile_count(const GemmProblem& p, int t) {
   return cdiv(p.m, kTiles[t].bm) * cdiv(p.n, kTiles[t].bn) * p.batch;
 }
@@ -67,10 +71,10 @@ int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, i
              bool partial_round_rule) {
   constexpr int64_t kCUs = 256;
   const int64_t tb = count(ps, big);
-  if (4 * tb >= 3 * kCUs && !(partial_round_rule && k <= 1024 && tb % kCUs != 0)) return big;
+  if (4 * tb >= 3 * kCUs && !(partial_round_rule && (k <= 512 || (k <= 1024 && tb % kCUs != 0)))) return big;
   const int64_t t1 = count(ps, 7);
   if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 7;
-  return 2;
+  return 8;
 }
 
 // Large launches take the four-wave 256x256 tile without a bias and the

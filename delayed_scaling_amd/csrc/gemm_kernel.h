@@ -67,16 +67,16 @@ typedef void (*GemmPairFn)(GemmKArgs, GemmKArgs, int);
 
 // Kernel pickers, one per translation unit.  tile indexes the family of
 // gemm.hip (0: 256x256 four waves, 1: 128x128, 2: 64x64, 3: 256x128,
-// 4: 128x256, 5 / 6: 256x256 eight waves as 2x4 / 4x2, 7: 128x128 on
-// 128-byte K units); fa / fb are the operand formats (0 E4M3, 1 E5M2).
-// "large" covers tiles 0, 5 and 6, "small" tiles 1 to 4 and 7.
+// 4: 128x256, 5 / 6: 256x256 eight waves as 2x4 / 4x2, 7 / 8: 128x128 /
+// 64x64 on 128-byte K units); fa / fb are the operand formats (0 E4M3,
+// 1 E5M2).  "large" covers tiles 0, 5 and 6, "small" tiles 1 to 4, 7 and 8.
 GemmFn gemm_fn_nt_large(int tile, int fa, int fb);
 GemmFn gemm_fn_nt_small(int tile, int fa, int fb);
 GemmFn gemm_fn_nn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_nn_small(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_small(int tile, int fa, int fb);
-// The fused NN + TN pair (a layer's dX and dW) for tiles 1, 2, 6 and 7.
+// The fused NN + TN pair (a layer's dX and dW) for tiles 1, 2, 6, 7 and 8.
 GemmPairFn gemm_pair_fn(int tile, int fa, int fb);
 
 namespace {
@@ -1011,7 +1011,7 @@ template <bool A_KC, bool B_KC, int FA, int FB, int R>
 __device__ __forceinline__ void gemm_body_u128(const GemmKArgs& p, lds_char_t* smem, int wg, int G) {
   constexpr int BM = R, BN = R, NW = 4, kThreads = 256;
   constexpr int WM = R / 2, WN = R / 2, TM = WM / 32, TN = WN / 32, NM = TM * TN, NF = TM + TN;
-  constexpr int kFragMfmas = 3 * NM / 4;
+  constexpr int kFragMfmas = NM >= 4 ? 3 * NM / 4 : NM;   // (one MFMA per wave: its reads follow it)
   using Loader = UnitLoader<NW, A_KC, B_KC, R>;
   constexpr int SLOT = Loader::SLOT, LPS = Loader::LPS;
 
@@ -1170,6 +1170,14 @@ __global__ __launch_bounds__(256, 2) void gemm_u128s_kernel(GemmKArgs p) {
   gemm_body_u128<A_KC, B_KC, FA, FB, 128>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
 }
 
+// And on a 64x64 tile (each wave a 32x32 block; five 8 KiB slots, four
+// workgroups per CU).
+template <bool A_KC, bool B_KC, int FA, int FB>
+__global__ __launch_bounds__(256, 4) void gemm_u128t_kernel(GemmKArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 64 * kKU];
+  gemm_body_u128<A_KC, B_KC, FA, FB, 64>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
+}
+
 // A layer's dX and dW in one launch on that tile (workgroups [0, g0) the
 // first problem, the rest the second, as in gemm_pair_kernel below).
 template <bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1, int FA, int FB>
@@ -1180,6 +1188,17 @@ __global__ __launch_bounds__(256, 2) void gemm_pair_u128s_kernel(GemmKArgs p0, G
     gemm_body_u128<A_KC0, B_KC0, FA, FB, 128>(p0, (lds_char_t*)smem_raw, wg, g0);
   else
     gemm_body_u128<A_KC1, B_KC1, FA, FB, 128>(p1, (lds_char_t*)smem_raw, wg - g0, (int)gridDim.x - g0);
+}
+
+// The same on the 64x64 unit tile.
+template <bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1, int FA, int FB>
+__global__ __launch_bounds__(256, 4) void gemm_pair_u128t_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 64 * kKU];
+  const int wg = (int)blockIdx.x;
+  if (wg < g0)
+    gemm_body_u128<A_KC0, B_KC0, FA, FB, 64>(p0, (lds_char_t*)smem_raw, wg, g0);
+  else
+    gemm_body_u128<A_KC1, B_KC1, FA, FB, 64>(p1, (lds_char_t*)smem_raw, wg - g0, (int)gridDim.x - g0);
 }
 
 // Two independent problems in one launch (a layer's dX and dW): workgroups
@@ -1230,6 +1249,14 @@ GemmFn pick_u128s(int fa, int fb) {
 }
 
 template <bool AKC, bool BKC>
+GemmFn pick_u128t(int fa, int fb) {
+  if (fa == 0 && fb == 0) return gemm_u128t_kernel<AKC, BKC, 0, 0>;
+  if (fa == 1 && fb == 0) return gemm_u128t_kernel<AKC, BKC, 1, 0>;
+  if (fa == 0 && fb == 1) return gemm_u128t_kernel<AKC, BKC, 0, 1>;
+  return gemm_u128t_kernel<AKC, BKC, 1, 1>;
+}
+
+template <bool AKC, bool BKC>
 GemmFn pick_large(int tile, int fa, int fb) {
   switch (tile) {
     case 5: return pick_fmt<256, 256, 2, 4, 4, 1, AKC, BKC>(fa, fb);
@@ -1249,6 +1276,7 @@ GemmFn pick_small(int tile, int fa, int fb) {
     case 2: return pick_fmt<64, 64, 2, 2, 4, 4, AKC, BKC>(fa, fb);
     case 3: return pick_fmt<256, 128, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
     case 7: return pick_u128s<AKC, BKC>(fa, fb);
+    case 8: return pick_u128t<AKC, BKC>(fa, fb);
     default: return pick_fmt<128, 256, 2, 2, 3, kOccRect, AKC, BKC>(fa, fb);
   }
 }

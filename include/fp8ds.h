@@ -274,8 +274,8 @@ int fp8_mm(const fp8_mm_args* args, void* stream);
 
 /* fp8_mm with the workgroup tile forced: tile = index into the tile family
  * (M x N: 0: 256x256, 1: 128x128, 2: 64x64, 3: 256x128, 4: 128x256, 5 and 6:
- * 256x256 with eight waves, 7: 128x128 on 128-byte K units), -1 or any index
- * outside 0..7 = the automatic choice.  Every tile accumulates each output over K in the same order, so
+ * 256x256 with eight waves, 7 and 8: 128x128 and 64x64 on 128-byte K units),
+ * -1 or any index outside 0..8 = the automatic choice.  Every tile accumulates each output over K in the same order, so
  * all tiles give the same bits; for tests and tuning sweeps. */
 int fp8_mm_with_tile(const fp8_mm_args* args, int tile, void* stream);
 

@@ -26,7 +26,7 @@ from test_gpu_gemm import FINITE, scale_tensor
 pytestmark = pytest.mark.gpu
 
 ONE = {oracle.E4M3: 0x38, oracle.E5M2: 0x3C}      # the code of 1.0 in each format
-TILES = ["auto", "256x256", "128x128", "64x64", "256x256w8", "128x128u"]
+TILES = ["auto", "256x256", "128x128", "64x64", "256x256w8", "128x128u", "64x64u"]
 SCALES = [(1.0, 1.0), (0.75, 0.125)]               # alpha 1 and 0.09375 = 3 * 2^-5
 
 

@@ -75,7 +75,7 @@ def run_case(ds, layout, fa, fb, m, n, k, batch=1, bcast_b=False, bias_kind=None
     return got, ref
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u", "64x64u"])
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 @pytest.mark.parametrize("fa,fb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_layouts_formats_tiles_ragged(tile, layout, fa, fb):
@@ -87,7 +87,7 @@ def test_layouts_formats_tiles_ragged(tile, layout, fa, fb):
     run_case(ds, LAYOUTS[layout], fa, fb, 130, 90, 200, tile=tile, pad_ld=16, seed=8)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u", "64x64u"])
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_workgroups_running_several_tiles(tile, layout):
     """Grids of 1, 3 and 8 workgroups: each workgroup runs many output tiles
@@ -104,7 +104,7 @@ def test_workgroups_running_several_tiles(tile, layout):
              grid=8)                                                                        # 2 stages, batches
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u"])
+@pytest.mark.parametrize("tile", ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u", "64x64u"])
 @pytest.mark.parametrize("layout", ["NT", "NN", "TN"])
 def test_epilogue_through_lds(tile, layout):
     """No bias, so every block inside C is stored through LDS: batches, a
@@ -122,7 +122,7 @@ def test_epilogue_through_lds(tile, layout):
 def test_small_integer_products_bit_exact(layout):
     ds = require_gpu()
     codes = np.array([0x00, 0x38, 0x40, 0xB8, 0xC0], np.uint8)   # 0, +-1, +-2
-    for tile in ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u"]:
+    for tile in ["256x256", "128x128", "64x64", "256x128", "128x256", "256x256w8n", "256x256w8", "128x128u", "64x64u"]:
         got, ref = run_case(ds, LAYOUTS[layout], 0, 0, 200, 136, 64, tile=tile, codes=codes, sa=1.0, sb=1.0, seed=3)
         assert np.array_equal(got, ref)
 
@@ -148,7 +148,7 @@ def test_deterministic_per_tile():
     m, n, k = 512, 384, 1024
     a = to_dev_u8(random_codes((m * k,), 20, FINITE[0]))
     b = to_dev_u8(random_codes((n * k,), 21, FINITE[0]))
-    for tile in ["256x256", "128x128", "64x64", "256x256w8", "128x128u"]:
+    for tile in ["256x256", "128x128", "64x64", "256x256w8", "128x128u", "64x64u"]:
         o1 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile)
         o2 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile)
         o3 = ds.fp8_mm(a, b, 0, 0, oracle.NT, m, n, k, scale_tensor(0.01), scale_tensor(0.01), tile=tile,
