@@ -836,7 +836,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p, lds_char_t* smem, 
 }
 
 // ---------------------------------------------------------------------------
-// The four-wave 256x256 tile on load units of 128 K bytes.
+// The four-wave 256x256 tile on load units of 128 K bytes (the body is a
+// template over the tile size R, which also runs 128x128 and 64x64 tiles;
+// the figures below are those of R = 256).
 //
 // An LDS-direct load that covers 128 contiguous bytes of each of 8 rows moves
 // more bytes per cycle through the CU's address unit than one that covers 64
@@ -889,7 +891,7 @@ __device__ __forceinline__ v8i frag_k128(const lds_char_t* slot, int base, int l
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// The same fragment from a crosswise slot [128 k][256 B]: half h is k rows
+// The same fragment from a crosswise slot [128 k][R B]: half h is k rows
 // 64 h .. 64 h + 63, read as in the general kernel.
 template <bool KC, int R>
 __device__ __forceinline__ v8i frag_u128(const lds_char_t* slot, int base, int lane, int h) {
@@ -899,7 +901,9 @@ __device__ __forceinline__ v8i frag_u128(const lds_char_t* slot, int base, int l
 
 // Load l of a wave covers slots i = (l * NW + wave) * 64 + lane: for a
 // K-contiguous operand rows 32 l + 8 wave + lane / 8, chunk lane % 8; for a
-// crosswise one k rows 16 l + 4 wave + lane / 16, chunk lane % 16.  The
+// crosswise one (R-byte k rows of CH = R / 16 chunks, KR = 64 / CH of them
+// per load and wave) k rows NW KR l + KR wave + lane / CH, chunk lane % CH
+// (R = 256: 16 l + 4 wave + lane / 16, chunk lane % 16).  The
 // swizzle depends only on the row bits that l leaves alone, so a lane's byte
 // offset is base + l * step with one per-lane base and a uniform step.
 // Rows of a K-contiguous operand past M (N) start past the end of the
@@ -988,7 +992,7 @@ struct UnitLoader {
 // last unit in one operand's slot, over whatever the loads brought there
 // (bytes of the operand past K, or zeros past its end): in a K-contiguous
 // slot bytes kin .. 127 of every row (chunk c of row r at c ^ swz_k128(r)),
-// in a crosswise slot the 256-byte k rows kin .. 127.
+// in a crosswise slot the R-byte k rows kin .. 127.
 template <bool KC, int kThreads, int R>
 __device__ __forceinline__ void zero_k_tail_slot(lds_char_t* slot, int kin) {
   const v4i z = v4i{0, 0, 0, 0};
