@@ -46,8 +46,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Tile choice by grid size, from per-shape timings on 256 CUs:
 //  * a 256x256 tile when its grid fills at least three quarters of the CUs,
-//    except when K <= 1024 and its last round of tiles is partial: there the 128x128 tile on 128-byte K units, two workgroups per
-//    CU, ends sooner (4096x3072x1024, 192 tiles: 15.2 against 17.8 us;
+//    except when K <= 1024 and its last round of tiles is partial: there
+//    the 128x128 tile on 128-byte K units, two workgroups per CU, ends
+//    sooner (4096x3072x1024, 192 tiles: 15.2 against 17.8 us;
 //    8192x3072x1024, 384 tiles: 25.5 against 30.9 us; with a bias 16.7 and
 //    28.9 against 20.6 and 34.9 us), while on whole rounds the two are level
 //    and with K = 4096 the 256x256 tile is clearly faster (4096^3: 50 against
@@ -67,11 +68,10 @@ int64_t tile_count(const GemmProblem& p, int t) {
 }
 
 // The rule over a launch's total tile count and (shortest) K.
-int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k, int big,
-             bool partial_round_rule) {
+int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, int64_t k, int big) {
   constexpr int64_t kCUs = 256;
   const int64_t tb = count(ps, big);
-  if (4 * tb >= 3 * kCUs && !(partial_round_rule && (k <= 512 || (k <= 1024 && tb % kCUs != 0)))) return big;
+  if (4 * tb >= 3 * kCUs && !(k <= 512 || (k <= 1024 && tb % kCUs != 0))) return big;
   const int64_t t1 = count(ps, 7);
   if (t1 >= kCUs || (2 * t1 >= kCUs && k >= 2048)) return 7;
   return 8;
@@ -80,8 +80,7 @@ int tile_for(int64_t (*count)(const GemmProblem*, int), const GemmProblem* ps, i
 // Large launches take the four-wave 256x256 tile without a bias and the
 // eight-wave one, which stages its bias epilogue through LDS, with one.
 int choose_tile(const GemmProblem& p) {
-  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6,
-                  true);
+  return tile_for([](const GemmProblem* q, int t) { return tile_count(*q, t); }, &p, p.k, p.bias_kind == 0 ? 0 : 6);
 }
 
 // For a fused pair: the same rule over both problems' tiles and the shorter K
@@ -92,7 +91,7 @@ int choose_tile(const GemmProblem& p) {
 // as one launch instead of two) from 3.53-3.59 to 3.50-3.52 ms.
 int choose_pair_tile(const GemmProblem (&pp)[2]) {
   return tile_for([](const GemmProblem* q, int t) { return tile_count(q[0], t) + tile_count(q[1], t); }, pp,
-                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6, true);
+                  pp[0].k < pp[1].k ? pp[0].k : pp[1].k, 6);
 }
 
 // Workgroups of one kernel that fit on the device at once (CUs x occupancy),
