@@ -104,6 +104,10 @@ def lib():
         L.fp8_mm_with_grid.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.fp8_mm_pair.restype = ctypes.c_int
         L.fp8_mm_pair.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.fp8_mm_tile.restype = ctypes.c_int
+        L.fp8_mm_tile.argtypes = [ctypes.c_void_p]
+        L.fp8_mm_pair_tile.restype = ctypes.c_int
+        L.fp8_mm_pair_tile.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fp8_quantize_ex.restype = i32
         L.fp8_quantize_ex.argtypes = [vp, i64, i32, i32, vp, vp, vp]

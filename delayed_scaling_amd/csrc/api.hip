@@ -353,4 +353,22 @@ int fp8_mm_pair(const fp8_mm_args* first, const fp8_mm_args* second, void* strea
   return launch_gemm_pair(p[0], p[1], s);
 }
 
+int fp8_mm_tile(const fp8_mm_args* a) {
+  GemmProblem p{};
+  bool empty = false;
+  if (const int st = check_mm(a, &p, &empty)) return st;
+  return empty ? FP8DS_TILE_NONE : gemm_tile(p);
+}
+
+int fp8_mm_pair_tile(const fp8_mm_args* first, const fp8_mm_args* second) {
+  GemmProblem p[2]{};
+  bool empty[2] = {false, false};
+  if (const int st = check_mm(first, &p[0], &empty[0])) return st;
+  if (const int st = check_mm(second, &p[1], &empty[1])) return st;
+  if (empty[0] && empty[1]) return FP8DS_TILE_NONE;
+  if (empty[0] || empty[1]) return FP8DS_TILE_SEPARATE;
+  const int t = gemm_pair_tile(p[0], p[1]);
+  return t < 0 ? FP8DS_TILE_SEPARATE : t;
+}
+
 }  // extern "C"

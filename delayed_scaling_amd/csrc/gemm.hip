@@ -24,7 +24,7 @@ struct TileCfg {
 // four waves runs one workgroup per CU (4 LDS stages, 128 KiB), each wave a
 // 128x128 block: the large-problem tile, as it reads the fewest LDS bytes per
 // MFMA; the eight-wave 256x256 tiles give every SIMD two waves of a 128x64 /
-// 64x128 block (the pair kernel's large tile); 256x128 / 128x256 run two
+// 64x128 block (the large tile of a GEMM with a bias); 256x128 / 128x256 run two
 // workgroups per CU (3 stages, 72 KiB each);
 // 128x128 and 64x64 serve problems too small to fill the chip; the 128x128
 // and 64x64 tiles on 128-byte K units (five 16 / 8 KiB slots, two / four
@@ -84,7 +84,8 @@ int choose_tile(const GemmProblem& p) {
 }
 
 // For a fused pair: the same rule over both problems' tiles and the shorter K
-// (the pair kernel has the eight-wave 256x256 tile).  The partial-round
+// (its 256x256 answer, the eight-wave tile, sends the two out as separate
+// launches: gemm_pair_tile below).  The partial-round
 // exception holds for pairs too: the 12-layer step at 2048 tokens (whose MLP
 // down-projection pair has 192 tiles of 256x256 and K = 1024) went from
 // 2.58-2.59 to 2.50-2.52 ms, at 4096 tokens (that pair, 320 tiles, then runs
@@ -180,19 +181,24 @@ int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hip
   return check_launch("gemm_kernel");
 }
 
-int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
-  if (!(p0.layout == 1 && p1.layout == 2 && p0.fmt_a == p1.fmt_a && p0.fmt_b == p1.fmt_b)) {
-    const int st = launch_gemm(p0, -1, 0, stream);
-    return st ? st : launch_gemm(p1, -1, 0, stream);
-  }
+int gemm_tile(const GemmProblem& p) { return choose_tile(p); }
+
+int gemm_pair_tile(const GemmProblem& p0, const GemmProblem& p1) {
+  if (!(p0.layout == 1 && p1.layout == 2 && p0.fmt_a == p1.fmt_a && p0.fmt_b == p1.fmt_b)) return -1;
   const GemmProblem pp[2] = {p0, p1};
   const int t = choose_pair_tile(pp);
-  // A problem that takes the four-wave 256x256 tile on its own runs faster
-  // there than in the pair kernel's eight-wave tile, by at least what the
-  // second launch costs (dX 8192x4096x1024 + dW 1024x4096x8192: 88.7 us as
-  // two launches, 97.2 us as one; at 4096 tokens the two are level).  Every
-  // tile gives the same bits, so the outputs do not depend on the choice.
-  if (t == 6 && (choose_tile(p0) == 0 || choose_tile(p1) == 0)) {
+  // A pair big enough for the eight-wave 256x256 tile runs faster as two
+  // launches, each on its own tile (graph-replayed, one box: dX 8192x1024x4096
+  // + dW 4096x1024x8192 69-76 us as two, 78-88 us as one; at 11264 tokens
+  // 97-99 against 109-112 us), so only the unit tiles run pairs.  Every tile
+  // gives the same bits, so the outputs do not depend on the choice.
+  if (t == 6) return -1;
+  return t;
+}
+
+int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream) {
+  const int t = gemm_pair_tile(p0, p1);
+  if (t < 0) {
     const int st = launch_gemm(p0, -1, 0, stream);
     return st ? st : launch_gemm(p1, -1, 0, stream);
   }

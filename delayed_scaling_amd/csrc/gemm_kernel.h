@@ -76,7 +76,7 @@ GemmFn gemm_fn_nn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_nn_small(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_large(int tile, int fa, int fb);
 GemmFn gemm_fn_tn_small(int tile, int fa, int fb);
-// The fused NN + TN pair (a layer's dX and dW) for tiles 1, 2, 6, 7 and 8.
+// The fused NN + TN pair (a layer's dX and dW) on tile 7 or 8.
 GemmPairFn gemm_pair_fn(int tile, int fa, int fb);
 
 namespace {
@@ -1182,8 +1182,12 @@ __global__ __launch_bounds__(256, 4) void gemm_u128t_kernel(GemmKArgs p) {
   gemm_body_u128<A_KC, B_KC, FA, FB, 64>(p, (lds_char_t*)smem_raw, (int)blockIdx.x, (int)gridDim.x);
 }
 
-// A layer's dX and dW in one launch on that tile (workgroups [0, g0) the
-// first problem, the rest the second, as in gemm_pair_kernel below).
+// Two independent problems in one launch (a layer's dX and dW) on that tile:
+// workgroups [0, g0) run the first, the rest the second, each as a grid of
+// its own.  The two share the tile, the formats and the LDS of a workgroup;
+// only the operand orientations differ.  g0 is a multiple of 8 whenever the
+// first problem's workgroups run more than one tile each, so the second keeps
+// the tile-to-XCD mapping of a launch of its own.
 template <bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1, int FA, int FB>
 __global__ __launch_bounds__(256, 2) void gemm_pair_u128s_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
   __shared__ __attribute__((aligned(1024))) char smem_raw[kUSlots * 128 * kKU];
@@ -1203,24 +1207,6 @@ __global__ __launch_bounds__(256, 4) void gemm_pair_u128t_kernel(GemmKArgs p0, G
     gemm_body_u128<A_KC0, B_KC0, FA, FB, 64>(p0, (lds_char_t*)smem_raw, wg, g0);
   else
     gemm_body_u128<A_KC1, B_KC1, FA, FB, 64>(p1, (lds_char_t*)smem_raw, wg - g0, (int)gridDim.x - g0);
-}
-
-// Two independent problems in one launch (a layer's dX and dW): workgroups
-// [0, g0) run the first, the rest the second, each as a grid of its own.  The
-// two share the tile, the formats and the LDS of a workgroup; only the
-// operand orientations differ.  g0 is a multiple of 8 whenever the first
-// problem's workgroups run more than one tile each, so the second keeps the
-// tile-to-XCD mapping of a launch of its own.
-template <int BM, int BN, int WGM, int WGN, int NBUF, int OCC, bool A_KC0, bool B_KC0, bool A_KC1, bool B_KC1,
-          int FA, int FB>
-__global__ __launch_bounds__(64 * WGM * WGN, OCC) void gemm_pair_kernel(GemmKArgs p0, GemmKArgs p1, int g0) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[smem_bytes<BM, BN, NBUF>()];
-  const int wg = (int)blockIdx.x;
-  if (wg < g0)
-    gemm_body<BM, BN, WGM, WGN, NBUF, A_KC0, B_KC0, FA, FB>(p0, (lds_char_t*)smem_raw, wg, g0);
-  else
-    gemm_body<BM, BN, WGM, WGN, NBUF, A_KC1, B_KC1, FA, FB>(p1, (lds_char_t*)smem_raw, wg - g0,
-                                                              (int)gridDim.x - g0);
 }
 
 // ---------------------------------------------------------------------------

@@ -53,4 +53,9 @@ int launch_gemm(const GemmProblem& p, int tile_override, int max_workgroups, hip
 // formats (a layer's dX and dW), else two launches in order.
 int launch_gemm_pair(const GemmProblem& p0, const GemmProblem& p1, hipStream_t stream);
 
+// The tile launch_gemm picks for p, and the one launch_gemm_pair runs a pair
+// on (-1: two launches).  Host arithmetic only.
+int gemm_tile(const GemmProblem& p);
+int gemm_pair_tile(const GemmProblem& p0, const GemmProblem& p1);
+
 }  // namespace fp8ds

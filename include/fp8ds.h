@@ -301,6 +301,23 @@ int fp8_mm_with_grid(const fp8_mm_args* args, int tile, int max_workgroups, void
  * zero) is skipped. */
 int fp8_mm_pair(const fp8_mm_args* first, const fp8_mm_args* second, void* stream);
 
+/* The tile fp8_mm would run these arguments on (an index of the tile family,
+ * as fp8_mm_with_tile takes it), FP8DS_TILE_NONE when it would launch nothing
+ * (m or n is 0), or the negative status fp8_mm would return for them.  Host
+ * arithmetic only: no device is needed and nothing is launched; the pointers
+ * are checked as fp8_mm checks them but never read.  For tests of the
+ * automatic tile choice and for tuning (not a step of the method). */
+#define FP8DS_TILE_NONE 64
+#define FP8DS_TILE_SEPARATE 65
+int fp8_mm_tile(const fp8_mm_args* args);
+
+/* The same for fp8_mm_pair: the tile of the one launch that runs both
+ * problems, FP8DS_TILE_SEPARATE when they go out as separate fp8_mm launches
+ * (each on the tile fp8_mm_tile reports for it; also when exactly one is
+ * empty), FP8DS_TILE_NONE when both are empty, or the negative status of the
+ * first invalid argument set (the pair's overlap checks are not made). */
+int fp8_mm_pair_tile(const fp8_mm_args* first, const fp8_mm_args* second);
+
 /* The library's own error report (not a step of the method): a message
  * describing the last non-zero status returned on the calling thread, kept in
  * thread-local storage until that thread's next failing call.  The pointer is

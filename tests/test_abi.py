@@ -268,3 +268,71 @@ def test_packed_structs_match_the_ctypes_layout():
     jv = [0x8000, 4096, 0x9000, 0xA000, 0xB000]
     assert ds._QJOB.size == ctypes.sizeof(ds._QuantJob)
     assert ds._QJOB.pack(*jv) == bytes(ds._QuantJob(*jv))
+
+
+def _mm_query_args(layout, m, n, k, batch=1, bias=False, fa=0):
+    """fp8_mm arguments of a dense problem at far-apart, aligned addresses
+    (the tile query checks the pointers as fp8_mm does but never reads them)."""
+    args = ds._MmArgs()
+    args.a, args.b, args.c = 1 << 40, 2 << 40, 3 << 40
+    args.a_scale_inv, args.b_scale_inv = 4 << 40, 4 << 40
+    args.fmt_a, args.fmt_b, args.layout = fa, 0, layout
+    args.m, args.n, args.k, args.batch = m, n, k, batch
+    a_rows, a_cols = (k, m) if layout == 2 else (m, k)
+    b_rows, b_cols = (n, k) if layout == 0 else (k, n)
+    args.lda, args.ldb, args.ldc = a_cols, b_cols, n
+    args.stride_a, args.stride_b, args.stride_c = a_rows * a_cols, b_rows * b_cols, m * n
+    if bias:
+        args.bias_kind, args.bias = 1, 5 << 40
+    return args
+
+
+TILE_NONE, TILE_SEPARATE = 64, 65
+
+
+@pytest.mark.parametrize("shape,bias,tile", [
+    ((0, 8192, 8192, 8192, 1), False, 0),     # the bench GEMM: four-wave 256x256
+    ((0, 8192, 8192, 8192, 1), True, 6),      # with a bias: the eight-wave 256x256 tile
+    ((0, 4096, 3072, 1024, 1), False, 7),     # K <= 1024, partial last round of 256x256 tiles
+    ((0, 8192, 3072, 1024, 1), True, 7),      # the same with a bias
+    ((0, 4096, 4096, 1024, 1), False, 0),     # one whole round of 256x256 tiles
+    ((0, 4096, 4096, 4096, 1), False, 0),
+    ((0, 512, 512, 512, 64), False, 7),       # K <= 512: the 128x128 unit tile over whole rounds
+    ((1, 2048, 1024, 4096, 1), False, 7),     # 128 tiles of 128x128 with K >= 2048
+    ((0, 4096, 1024, 1024, 1), False, 7),     # 256 tiles of 128x128
+    ((0, 2048, 1024, 1024, 1), False, 8),     # 128 tiles with K < 2048: the 64x64 unit tile
+    ((0, 1024, 1536, 2048, 1), False, 8),
+    ((2, 1024, 1024, 4096, 1), False, 8),
+    ((0, 0, 64, 64, 1), False, TILE_NONE),    # empty: nothing launched
+])
+def test_tile_choice(L, shape, bias, tile):
+    """The automatic tile choice at the shapes its rules were measured on."""
+    layout, m, n, k, batch = shape
+    assert L.fp8_mm_tile(ctypes.byref(_mm_query_args(layout, m, n, k, batch, bias))) == tile
+
+
+@pytest.mark.parametrize("t,n_in,n_out,tile", [
+    (4096, 1024, 1024, 7),             # the 12-layer step's O projection at 4096 tokens
+    (4096, 4096, 1024, 7),             # its MLP down projection: 320 tiles of 256x256, K = 1024, partial round
+    (4096, 1024, 4096, 7),             # its MLP up projection
+    (2048, 1024, 1024, 8),             # the O projection at 2048 tokens
+    (8192, 1024, 4096, TILE_SEPARATE),  # the rule's eight-wave 256x256 answer: two launches
+    (11264, 1024, 11264, TILE_SEPARATE),
+])
+def test_pair_tile_choice(L, t, n_in, n_out, tile):
+    """The pair's tile (dX = G W as NN, dW = G^T X as TN, E5M2 x E4M3), or
+    two separate launches."""
+    dx = _mm_query_args(1, t, n_in, n_out, fa=1)
+    dw = _mm_query_args(2, n_out, n_in, t, fa=1)
+    assert L.fp8_mm_pair_tile(ctypes.byref(dx), ctypes.byref(dw)) == tile
+
+
+def test_tile_query_checks_arguments(L):
+    args = _mm_query_args(0, 256, 256, 256)
+    args.layout = 7
+    assert L.fp8_mm_tile(ctypes.byref(args)) == -1
+    nt0 = _mm_query_args(0, 256, 256, 256)
+    nt1 = _mm_query_args(0, 128, 256, 256)
+    assert L.fp8_mm_pair_tile(ctypes.byref(nt0), ctypes.byref(nt1)) == TILE_SEPARATE   # not NN + TN
+    empty = _mm_query_args(1, 0, 256, 256)
+    assert L.fp8_mm_pair_tile(ctypes.byref(empty), ctypes.byref(empty)) == TILE_NONE

@@ -59,13 +59,14 @@ def test_pair_ragged_matches_oracle_and_single_calls(fa, fb):
 
 
 @pytest.mark.parametrize("t,n_in,n_out", [(2048, 1024, 3072), (2048, 1024, 1024), (2048, 4096, 1024),
-                                          (4096, 4096, 4096), (11264, 1024, 11264)])
+                                          (4096, 4096, 1024), (4096, 4096, 4096), (11264, 1024, 11264)])
 def test_pair_at_layer_shapes_equals_single_calls(t, n_in, n_out):
     """The linear layer's backward shapes, plus sampled entries against the
-    oracle.  At 4096 the dX problem takes the four-wave 256x256 tile on its
-    own, so the pair goes out as two launches; at 11264 neither does, and the
-    pair kernel runs its eight-wave 256x256 tile with more tiles than the
-    device holds at once, so its workgroups run several tiles each."""
+    oracle.  At 4096 x 4096 x 1024 the pair runs as one launch on the 128x128
+    unit tile with 1280 tiles, more than the device holds at once, so its
+    workgroups run several tiles each; at 4096 x 4096 x 4096 and at 11264 the
+    rule's tile for the pair is the eight-wave 256x256 one, so the two go out
+    as separate launches."""
     ds = require_gpu()
     sa, sb, sc = 0.011, 0.017, 0.023
     dx, hx = problem(oracle.NN, 1, 0, t, n_in, n_out, 30, sa, sb)
